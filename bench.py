@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA/HCA Compressor (THD gated-softmax pooling) on MI355X.
+
+One step = forward + backward of the Compressor over one THD pack (default:
+3 x 8192 tokens, head_dim 512, ratio 4, coff 2), i.e. every kernel of the
+path: forward, backward gradients (with the zero-ownership writes and dAPE
+partials) and the dAPE reduce.  Inputs are synthetic (seeded N(0,1) bf16
+kv/score/dout, N(0, 0.02) fp32 APE) and resident in HBM before timing.
+
+Cache protocol: the 256 MB last-level cache would hold a whole pack, so the
+timed region cycles through --sets independent buffer sets, running the
+forwards of a group of sets and then their backwards (as a training step
+does layer by layer); every kernel therefore reads inputs that at least
+~400 MB of other traffic has passed through since they were last touched.
+
+Prints ONE JSON line: value = algorithmic HBM bytes of the step / time per
+step (GB/s).  The per-kernel averages come from HIP events recorded on the
+launch stream inside the timed region; the roofline object is for the
+dominant kernel.  The CPU oracle is timed on the host as a baseline.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--sets S]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
+METRIC = "fwd+bwd µs/call and HBM GB/s (% of MI355X peak), 3x8192-tok d512 r4 c2"
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "gated_pooling_amd", "csrc", f) for f in
+                  ("csa_kernels.hip", "csa_api.cpp", "csa_launch.h")]
+
+
+def consumed_slots(cu, r, c, d):
+    """kv/score slots some window reads: (2 nb - 1) r d per segment at coff 2
+    (the first block has no previous half), nb r d at coff 1."""
+    total = 0
+    for s in range(len(cu) - 1):
+        nb = (cu[s + 1] - cu[s]) // r
+        if nb:
+            total += ((2 * nb - 1) if c == 2 else nb) * r * d
+    return total
+
+
+def algorithmic_bytes(cu, T, r, c, d, N):
+    """Bytes the method itself must move, per kernel: every consumed kv/score
+    slot read once, APE read, out written (forward); the same reads plus dout,
+    and dkv/dscore written in full (backward gradients); dAPE written
+    (reduce).  Workspace traffic (dAPE partials) is overhead, not counted."""
+    W = c * d
+    cons = consumed_slots(cu, r, c, d)
+    fwd = 2 * 2 * cons + 4 * r * W + 2 * N * d
+    grads = 2 * 2 * cons + 4 * r * W + 2 * N * d + 2 * 2 * T * W
+    reduce = 4 * r * W
+    return {"fwd": fwd, "bwd_grads": grads, "dape_reduce": reduce}
+
+
+def sources_digest():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    counters, or None if absent or taken on different kernel sources."""
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_digest():
+        return None
+    ent = rec.get("kernels", {}).get(workload, {}).get(kernel)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, N, kv, sc, ape, dout, budget_s):
+    """Time the CPU oracle (fp32 evaluation order, OpenMP over windows) on the
+    same pack: forward + backward, repeated until about budget_s seconds."""
+    import numpy as np
+
+    import oracle
+    from gated_pooling_amd import inputs
+
+    args = (inputs.bits(kv), inputs.bits(sc), ape.numpy(), list(wl.cu_seqlens), wl.total_tokens,
+            wl.ratio, wl.coff, wl.head_dim)
+    doutb = inputs.bits(dout)
+    out = np.zeros((N, wl.head_dim), np.uint16)
+    outs = oracle.bwd_outputs(wl.total_tokens, wl.ratio, wl.coff, wl.head_dim, N)
+    oracle.fwd_f32(*args, out=out)          # warm-up (page faults, caches)
+    oracle.bwd_f32(*args, doutb, outs=outs)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.fwd_f32(*args, out=out)
+        oracle.bwd_f32(*args, doutb, outs=outs)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 200:
+            break
+    return reps, el, oracle.num_threads()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--sets", type=int, default=5, help="rotating buffer sets (cold cache)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-warm", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (the Compressor path runs on a single "
+              "device; --gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_pooling_amd as G
+    from gated_pooling_amd import inputs
+
+    wname = args.workload or inputs.HEADLINE
+    wl = inputs.WORKLOADS[wname]
+    cu, T, r, c, d = list(wl.cu_seqlens), wl.total_tokens, wl.ratio, wl.coff, wl.head_dim
+    W, S = c * d, wl.num_segments
+    N = G.csa_compressor_total_comp(cu, r)
+    dev = torch.device("cuda:0")
+    G.lib()
+
+    kv, sc, ape, dout = inputs.make_tensors(wl, N)
+    fwd_ws = G.csa_compressor_fwd_workspace_size(r, c, d, S, T, N)
+    bwd_ws = G.csa_compressor_bwd_workspace_size(r, c, d, S, T, N)
+    sets = []
+    for _ in range(max(1, args.sets)):
+        st = {
+            "kv": kv.to(dev), "sc": sc.to(dev), "ape": ape.to(dev), "dout": dout.to(dev),
+            "cu": torch.tensor(cu, dtype=torch.int32, device=dev),
+            "out": torch.empty(N, d, dtype=torch.bfloat16, device=dev),
+            "dkv": torch.empty(T, W, dtype=torch.bfloat16, device=dev),
+            "dsc": torch.empty(T, W, dtype=torch.bfloat16, device=dev),
+            "dape": torch.empty(r, W, dtype=torch.float32, device=dev),
+            "fws": G.workspace(fwd_ws, dev), "bws": G.workspace(bwd_ws, dev),
+        }
+        st["p"] = {k: ctypes.c_void_p(v.data_ptr()) for k, v in st.items() if isinstance(v, torch.Tensor)}
+        sets.append(st)
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    L = G.lib()
+
+    def fwd(st):
+        p = st["p"]
+        rc = L.csa_compressor_fwd(p["kv"], p["sc"], p["ape"], p["cu"], S, T, N, r, c, d, p["out"], p["fws"],
+                                  st["fws"].numel(), sptr)
+        assert rc == 0, G.csa_last_error()
+
+    def grads(st):
+        p = st["p"]
+        rc = L.csa_compressor_bwd_grads(p["kv"], p["sc"], p["ape"], p["cu"], S, T, N, r, c, d, p["dout"], p["dkv"],
+                                        p["dsc"], p["bws"], st["bws"].numel(), sptr)
+        assert rc == 0, G.csa_last_error()
+
+    def reduce(st):
+        p = st["p"]
+        rc = L.csa_compressor_bwd_dape_reduce(r, c, d, S, T, N, p["dape"], p["bws"], st["bws"].numel(), sptr)
+        assert rc == 0, G.csa_last_error()
+
+    nsets = len(sets)
+
+    def run_steps(K, events=None):
+        """K steps in groups of nsets: the group's forwards, then its backwards."""
+        done = 0
+        while done < K:
+            grp = list(range(min(nsets, K - done)))
+            for j in grp:
+                if events is not None:
+                    events["fwd"][done + j][0].record(stream)
+                fwd(sets[j])
+                if events is not None:
+                    events["fwd"][done + j][1].record(stream)
+            for j in grp:
+                if events is not None:
+                    events["bwd_grads"][done + j][0].record(stream)
+                grads(sets[j])
+                if events is not None:
+                    events["bwd_grads"][done + j][1].record(stream)
+                    events["dape_reduce"][done + j][0].record(stream)
+                reduce(sets[j])
+                if events is not None:
+                    events["dape_reduce"][done + j][1].record(stream)
+            done += len(grp)
+
+    # warm-up, then the timed region
+    run_steps(max(args.warmup, 0))
+    torch.cuda.synchronize()
+    K = args.steps
+    mk = lambda: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]  # noqa: E731
+    events = {"fwd": mk(), "bwd_grads": mk(), "dape_reduce": mk()}
+    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    region[0].record(stream)
+    run_steps(K, events)
+    region[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / K
+    gpu_ms_per_step = region[0].elapsed_time(region[1]) / K
+
+    abytes = algorithmic_bytes(cu, T, r, c, d, N)
+    step_bytes = sum(abytes.values())
+    kern = {}
+    for name, evs in events.items():
+        us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+        avg = sum(us) / len(us)
+        kern[name] = {"avg_us": round(avg, 3), "min_us": round(min(us), 3),
+                      "algorithmic_bytes": abytes[name],
+                      "GBs": round(abytes[name] / (avg * 1e-6) / 1e9, 1)}
+    dom = max(kern, key=lambda k: kern[k]["avg_us"])
+    achieved = kern[dom]["GBs"]
+    traffic = load_traffic(dom, wname)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    warm = None
+    if not args.no_warm:
+        wev = {"fwd": [], "bwd_grads": [], "dape_reduce": []}
+        for _ in range(3):
+            fwd(sets[0]); grads(sets[0]); reduce(sets[0])  # noqa: E702
+        for _ in range(20):
+            for name, fn in (("fwd", fwd), ("bwd_grads", grads), ("dape_reduce", reduce)):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn(sets[0])
+                b.record(stream)
+                wev[name].append((a, b))
+        torch.cuda.synchronize()
+        warm = {k: round(sum(a.elapsed_time(b) for a, b in v) * 1e3 / len(v), 3) for k, v in wev.items()}
+
+    # context: a plain device-to-device copy of 512 MiB (torch's copy kernel)
+    src = torch.empty(256 * 2 ** 20, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 2 * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        reps, el, cores = cpu_baseline(wl, N, kv, sc, ape, dout, args.cpu_seconds)
+        cpu = {"value": round(step_bytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+               "sample": f"{reps} x (forward + backward) of the full {wname} pack, fp32-order C oracle, "
+                         f"{el:.1f} s", "ms_per_step": round(el * 1e3 / reps, 1)}
+
+    fwd_us = kern["fwd"]["avg_us"]
+    bwd_us = kern["bwd_grads"]["avg_us"] + kern["dape_reduce"]["avg_us"]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "io_dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wname, "cu_seqlens": cu if len(cu) <= 8 else f"{S} segments",
+                   "total_tokens": T, "total_comp": N, "ratio": r, "coff": c, "head_dim": d,
+                   "cache": f"cold ({nsets} rotating buffer sets)"},
+        "us_per_call": {"fwd": fwd_us, "bwd": round(bwd_us, 3), "fwd_bwd": round(fwd_us + bwd_us, 3),
+                        "step_wall": round(ms_per_step * 1e3, 3), "step_gpu": round(gpu_ms_per_step * 1e3, 3)},
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "step_algorithmic_bytes": step_bytes,
+        "kernels": kern,
+        "warm_us": warm,
+        "copy_kernel_GBs": round(copy_gbs, 1),
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

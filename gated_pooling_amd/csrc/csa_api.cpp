@@ -1,0 +1,448 @@
+// csa_api.cpp -- the C ABI of libcsa (include/csa.h): argument validation,
+// launch planning and dispatch to the gfx950 kernels.
+//
+// Validation and planning are pure host code and depend only on the problem
+// description and the tuning knobs below, never on the device, so every
+// rejection (including an undersized workspace) happens before any HIP call.
+//
+// Support envelope ([PR5984] = NVIDIA/Megatron-LM pull request 5984 page,
+// [PR710] = cudnn-frontend pull request 710 page): ratio in {2, 4}
+// ([PR710: What]), coff in {1, 2} ([PR5984: coff commit]); the size limits
+// total_tokens*coff*head_dim, total_comp*head_dim and ratio*coff*head_dim
+// below 2^31 each, and the rejection of total_comp > 0 with
+// total_tokens < ratio ([PR5984: review-feedback commit; PR710: What]).
+// head_dim must be a power of two in [2, 1024] in this build (the lane
+// layout splits a half-row into power-of-two chunks).
+//
+// Tuning knobs (environment, read once per process; every value is
+// validated and falls back to the default):
+//   CSA_FWD_COLS      output columns per lane in the forward (2, 4, 8)
+//   CSA_FWD_MAX_WGS   forward grid cap in workgroups of 256 threads
+//   CSA_BWD_COLS      output columns per lane in the backward (2, 4, 8)
+//   CSA_BWD_THREADS   backward workgroup size (256, 512, 1024)
+//   CSA_BWD_MAX_WGS   backward grid cap (main workgroups)
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/csa.h"
+#include "csa_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+csa_status_t fail(csa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+csa_status_t ok() {
+  g_err.clear();
+  return CSA_STATUS_SUCCESS;
+}
+
+struct Tuning {
+  int fwd_cols = 4;
+  int fwd_max_wgs = 2048;
+  int bwd_cols = 2;
+  int bwd_threads = 1024;
+  int bwd_max_wgs = 256;
+};
+
+int env_int(const char* name, int dflt, const int* allowed, int n_allowed, int lo, int hi) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  char* end = nullptr;
+  long x = strtol(v, &end, 10);
+  if (*end != '\0') return dflt;
+  if (allowed) {
+    for (int i = 0; i < n_allowed; ++i)
+      if (allowed[i] == x) return static_cast<int>(x);
+    return dflt;
+  }
+  return (x >= lo && x <= hi) ? static_cast<int>(x) : dflt;
+}
+
+const Tuning& tuning() {
+  static const Tuning t = [] {
+    Tuning d;
+    static const int cols[] = {2, 4, 8};
+    static const int threads[] = {256, 512, 1024};
+    d.fwd_cols = env_int("CSA_FWD_COLS", d.fwd_cols, cols, 3, 0, 0);
+    d.fwd_max_wgs = env_int("CSA_FWD_MAX_WGS", d.fwd_max_wgs, nullptr, 0, 1, 1 << 20);
+    d.bwd_cols = env_int("CSA_BWD_COLS", d.bwd_cols, cols, 3, 0, 0);
+    d.bwd_threads = env_int("CSA_BWD_THREADS", d.bwd_threads, threads, 3, 0, 0);
+    d.bwd_max_wgs = env_int("CSA_BWD_MAX_WGS", d.bwd_max_wgs, nullptr, 0, 1, 1 << 16);
+    return d;
+  }();
+  return t;
+}
+
+struct Problem {
+  int32_t ratio, coff, head_dim, S;
+  int64_t T, N;
+};
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int64_t x) {
+  int l = 0;
+  while ((int64_t{1} << l) < x) ++l;
+  return l;
+}
+uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+csa_status_t check_problem(const Problem& p) {
+  if (p.ratio != 2 && p.ratio != 4)
+    return fail(CSA_STATUS_NOT_SUPPORTED, "ratio must be 2 or 4 (got %d)", p.ratio);
+  if (p.coff != 1 && p.coff != 2)
+    return fail(CSA_STATUS_NOT_SUPPORTED, "coff must be 1 or 2 (got %d)", p.coff);
+  if (!is_pow2(p.head_dim) || p.head_dim < 2 || p.head_dim > 1024)
+    return fail(CSA_STATUS_NOT_SUPPORTED, "head_dim must be a power of two in [2, 1024] (got %d)", p.head_dim);
+  if (p.S < 0 || p.T < 0 || p.N < 0)
+    return fail(CSA_STATUS_INVALID_VALUE, "negative size: num_segments=%d total_tokens=%lld total_comp=%lld",
+                p.S, (long long)p.T, (long long)p.N);
+  const int64_t W = int64_t{p.coff} * p.head_dim;
+  const int64_t lim = int64_t{1} << 31;
+  if (p.T * W >= lim)
+    return fail(CSA_STATUS_NOT_SUPPORTED, "total_tokens*coff*head_dim must be below 2^31");
+  if (p.N * p.head_dim >= lim)
+    return fail(CSA_STATUS_NOT_SUPPORTED, "total_comp*head_dim must be below 2^31");
+  if (int64_t{p.ratio} * W >= lim)
+    return fail(CSA_STATUS_NOT_SUPPORTED, "ratio*coff*head_dim must be below 2^31");
+  if (p.N > 0 && p.T < p.ratio)
+    return fail(CSA_STATUS_INVALID_VALUE, "total_comp > 0 with total_tokens < ratio");
+  if (p.N * p.ratio > p.T)
+    return fail(CSA_STATUS_INVALID_VALUE, "total_comp*ratio exceeds total_tokens");
+  if (p.S == 0 && p.N != 0)
+    return fail(CSA_STATUS_INVALID_VALUE, "total_comp > 0 with no segments");
+  return ok();
+}
+
+// Workspace layout: [0, 256) header (int32 validity flag at 0);
+// then, for packs above kMaxLdsSegments, int32 offsets [S + 1];
+// then (backward) fp32 dAPE partials [partial_rows, ratio, W].
+struct Plan {
+  bool global_table;
+  uint64_t off_bytes;   // offsets section size
+  // forward
+  csa::LaunchShape fwd;
+  int fwd_log2_chunks;
+  uint64_t ws_fwd;
+  // backward
+  csa::LaunchShape bwd;
+  int bwd_log2_chunks;
+  uint32_t bwd_main_wgs;
+  uint32_t partial_rows;
+  uint32_t lds_table_words;
+  uint64_t partial_offset;
+  uint64_t ws_bwd;
+};
+
+constexpr uint64_t kHeaderBytes = 256;
+
+Plan make_plan(const Problem& p) {
+  const Tuning& tu = tuning();
+  Plan pl{};
+  const int64_t W = int64_t{p.coff} * p.head_dim;
+  pl.global_table = p.S > csa::kMaxLdsSegments;
+  pl.off_bytes = pl.global_table ? align_up(uint64_t(p.S + 1) * 4, 256) : 0;
+
+  // forward: one lane per (output row, chunk of C columns), grid-stride
+  {
+    const int C = p.head_dim < tu.fwd_cols ? p.head_dim : tu.fwd_cols;
+    const int64_t G = p.head_dim / C;
+    const int64_t lanes = p.N * G;
+    int64_t wgs = (lanes + csa::kFwdThreads - 1) / csa::kFwdThreads;
+    if (wgs > tu.fwd_max_wgs) wgs = tu.fwd_max_wgs;
+    if (G > csa::kFwdThreads) wgs = align_up(wgs, G / csa::kFwdThreads);  // lanes % G == 0
+    pl.fwd.grid = static_cast<uint32_t>(wgs);
+    pl.fwd.threads = csa::kFwdThreads;
+    pl.fwd.cols = C;
+    pl.fwd_log2_chunks = log2i(G);
+    const uint64_t table_words = pl.global_table ? 0 : 2 * (csa::kFwdThreads / 64) + 2 * uint64_t(p.S + 1);
+    pl.fwd.lds_bytes = table_words * 4;
+    pl.ws_fwd = pl.global_table ? kHeaderBytes + pl.off_bytes : 0;
+  }
+  // backward
+  {
+    const int C = p.head_dim < tu.bwd_cols ? p.head_dim : tu.bwd_cols;
+    const int NT = tu.bwd_threads;
+    const int64_t G = p.head_dim / C;
+    const int64_t lanes = p.N * G;
+    int64_t main = (lanes + NT - 1) / NT;
+    if (main > tu.bwd_max_wgs) main = tu.bwd_max_wgs;
+    const int64_t slices = G > NT ? G / NT : 1;
+    main = align_up(main, slices);  // lanes % G == 0 and whole partial rows
+    // zero-fill workgroups for rows of segments shorter than ratio and rows
+    // past cu[S]: at most total_tokens - total_comp*ratio rows qualify
+    const int64_t spare_rows = p.T - p.N * p.ratio;
+    int64_t zero = 0;
+    if (spare_rows > 0) {
+      const int64_t bytes = spare_rows * W * 2 * 2;
+      zero = (bytes + int64_t{NT} * 16 * 8 - 1) / (int64_t{NT} * 16 * 8);
+      if (zero < 1) zero = 1;
+      if (zero > 256) zero = 256;
+    }
+    if (main + zero == 0) zero = 1;  // someone must write the validity flag
+    pl.bwd.grid = static_cast<uint32_t>(main + zero);
+    pl.bwd.threads = NT;
+    pl.bwd.cols = C;
+    pl.bwd_log2_chunks = log2i(G);
+    pl.bwd_main_wgs = static_cast<uint32_t>(main);
+    pl.partial_rows = static_cast<uint32_t>(main / slices);
+    pl.lds_table_words = pl.global_table ? 0 : static_cast<uint32_t>(2 * (NT / 64) + 2 * (p.S + 1));
+    const int64_t wg_chunks = G < NT ? G : NT;
+    const uint64_t red_floats = uint64_t(p.coff) * p.ratio * wg_chunks * C;
+    pl.bwd.lds_bytes = (uint64_t(pl.lds_table_words) + red_floats) * 4;
+    pl.partial_offset = kHeaderBytes + pl.off_bytes;
+    pl.ws_bwd = pl.partial_offset + align_up(uint64_t(pl.partial_rows) * p.ratio * W * 4, 256);
+  }
+  return pl;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+csa_status_t check_ptr(const void* p, const char* name) {
+  if (!p) return fail(CSA_STATUS_INVALID_VALUE, "%s is null", name);
+  if (!aligned16(p)) return fail(CSA_STATUS_INVALID_VALUE, "%s is not 16-byte aligned", name);
+  return CSA_STATUS_SUCCESS;
+}
+
+csa::SegParams seg_params(const Problem& p, const Plan& pl, const int32_t* cu, void* ws) {
+  csa::SegParams sp{};
+  sp.cu = cu;
+  sp.T_cap = p.T;
+  sp.N = p.N;
+  sp.S = p.S;
+  sp.global_table = pl.global_table ? 1 : 0;
+  if (pl.global_table) {
+    sp.g_flag = reinterpret_cast<const int32_t*>(ws);
+    sp.g_off = reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + kHeaderBytes);
+  }
+  return sp;
+}
+
+csa_status_t after_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(CSA_STATUS_LAUNCH_FAILED, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+csa_status_t launch_scan_if_needed(const Problem& p, const Plan& pl, const int32_t* cu, void* ws,
+                                   hipStream_t stream) {
+  if (!pl.global_table) return CSA_STATUS_SUCCESS;
+  const csa::SegParams sp = seg_params(p, pl, cu, ws);
+  int32_t* flag = reinterpret_cast<int32_t*>(ws);
+  int32_t* off = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + kHeaderBytes);
+  if (!csa::launch_seg_scan(p.ratio, sp, off, flag, stream))
+    return fail(CSA_STATUS_NOT_SUPPORTED, "no scan kernel for ratio %d", p.ratio);
+  return after_launch("segment scan");
+}
+
+// Validation shared by the backward entry points.
+csa_status_t check_bwd_args(const Problem& pr, const Plan& pl, const void* kv, const void* score,
+                            const float* ape, const int32_t* cu, const void* dout, const void* dkv,
+                            const void* dscore, const void* workspace, size_t workspace_bytes) {
+  csa_status_t st;
+  if (pr.T > 0) {
+    if ((st = check_ptr(dkv, "dkv")) || (st = check_ptr(dscore, "dscore"))) return st;
+  }
+  if (pr.N > 0) {
+    if ((st = check_ptr(kv, "kv")) || (st = check_ptr(score, "score")) || (st = check_ptr(ape, "ape")) ||
+        (st = check_ptr(dout, "dout")))
+      return st;
+  }
+  // the backward always launches (it must zero its outputs), so cu is read
+  if (!cu) return fail(CSA_STATUS_INVALID_VALUE, "cu_seqlens is null");
+  if (reinterpret_cast<uintptr_t>(cu) & 3u) return fail(CSA_STATUS_INVALID_VALUE, "cu_seqlens is not 4-byte aligned");
+  if (workspace_bytes < pl.ws_bwd)
+    return fail(CSA_STATUS_WORKSPACE_TOO_SMALL, "backward needs %llu workspace bytes, got %llu",
+                (unsigned long long)pl.ws_bwd, (unsigned long long)workspace_bytes);
+  if ((st = check_ptr(workspace, "workspace"))) return st;
+  return CSA_STATUS_SUCCESS;
+}
+
+csa_status_t launch_bwd_grads(const Problem& pr, const Plan& pl, const void* kv, const void* score,
+                              const float* ape, const int32_t* cu, const void* dout, void* dkv, void* dscore,
+                              void* workspace, hipStream_t stream) {
+  csa_status_t st = launch_scan_if_needed(pr, pl, cu, workspace, stream);
+  if (st) return st;
+  csa::BwdParams bp{};
+  bp.seg = seg_params(pr, pl, cu, workspace);
+  bp.kv = static_cast<const uint16_t*>(kv);
+  bp.score = static_cast<const uint16_t*>(score);
+  bp.ape = ape;
+  bp.dout = static_cast<const uint16_t*>(dout);
+  bp.dkv = static_cast<uint16_t*>(dkv);
+  bp.dscore = static_cast<uint16_t*>(dscore);
+  bp.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.partial_offset);
+  bp.ws_flag = reinterpret_cast<int32_t*>(workspace);
+  bp.io_bytes = static_cast<uint32_t>(pr.T * pr.coff * pr.head_dim * 2);
+  bp.head_dim = pr.head_dim;
+  bp.log2_chunks = pl.bwd_log2_chunks;
+  bp.main_wgs = pl.bwd_main_wgs;
+  bp.partial_rows = pl.partial_rows;
+  bp.lds_table_words = pl.lds_table_words;
+  if (!csa::launch_bwd(pr.ratio, pr.coff, bp, pl.bwd, stream))
+    return fail(CSA_STATUS_NOT_SUPPORTED, "no backward kernel for this configuration");
+  return after_launch("backward");
+}
+
+csa_status_t launch_reduce(const Problem& pr, const Plan& pl, float* dape, void* workspace, hipStream_t stream) {
+  csa::ReduceParams rp{};
+  rp.partials = reinterpret_cast<const float*>(static_cast<char*>(workspace) + pl.partial_offset);
+  rp.dape = dape;
+  rp.ws_flag = reinterpret_cast<const int32_t*>(workspace);
+  rp.rows = pl.partial_rows;
+  rp.cols = static_cast<uint32_t>(pr.ratio * pr.coff * pr.head_dim);
+  csa::launch_dape_reduce(rp, stream);
+  return after_launch("dAPE reduce");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa_status_string(csa_status_t status) {
+  switch (status) {
+    case CSA_STATUS_SUCCESS: return "CSA_STATUS_SUCCESS";
+    case CSA_STATUS_INVALID_VALUE: return "CSA_STATUS_INVALID_VALUE";
+    case CSA_STATUS_NOT_SUPPORTED: return "CSA_STATUS_NOT_SUPPORTED";
+    case CSA_STATUS_WORKSPACE_TOO_SMALL: return "CSA_STATUS_WORKSPACE_TOO_SMALL";
+    case CSA_STATUS_LAUNCH_FAILED: return "CSA_STATUS_LAUNCH_FAILED";
+    case CSA_STATUS_DEVICE_ERROR: return "CSA_STATUS_DEVICE_ERROR";
+  }
+  return "CSA_STATUS_UNKNOWN";
+}
+
+const char* csa_last_error(void) { return g_err.c_str(); }
+
+int32_t csa_version(void) { return 100; }
+
+csa_status_t csa_compressor_total_comp(const int32_t* cu, int32_t S, int32_t ratio, int64_t* total_comp) {
+  if (!cu || !total_comp) return fail(CSA_STATUS_INVALID_VALUE, "null pointer");
+  if (S < 0 || ratio < 1) return fail(CSA_STATUS_INVALID_VALUE, "num_segments < 0 or ratio < 1");
+  if (cu[0] != 0) return fail(CSA_STATUS_INVALID_VALUE, "cu_seqlens[0] must be 0");
+  int64_t n = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    const int64_t L = int64_t{cu[s + 1]} - cu[s];
+    if (L < 0) return fail(CSA_STATUS_INVALID_VALUE, "cu_seqlens decreases at %d", s);
+    n += L / ratio;
+  }
+  *total_comp = n;
+  return ok();
+}
+
+csa_status_t csa_compressor_check_support(int32_t ratio, int32_t coff, int32_t head_dim, int32_t S,
+                                          int64_t total_tokens, int64_t total_comp) {
+  return check_problem(Problem{ratio, coff, head_dim, S, total_tokens, total_comp});
+}
+
+csa_status_t csa_compressor_fwd_workspace_size(int32_t ratio, int32_t coff, int32_t head_dim, int32_t S,
+                                               int64_t total_tokens, int64_t total_comp, size_t* bytes) {
+  if (!bytes) return fail(CSA_STATUS_INVALID_VALUE, "bytes is null");
+  const Problem pr{ratio, coff, head_dim, S, total_tokens, total_comp};
+  const csa_status_t st = check_problem(pr);
+  if (st) return st;
+  *bytes = make_plan(pr).ws_fwd;
+  return ok();
+}
+
+csa_status_t csa_compressor_bwd_workspace_size(int32_t ratio, int32_t coff, int32_t head_dim, int32_t S,
+                                               int64_t total_tokens, int64_t total_comp, size_t* bytes) {
+  if (!bytes) return fail(CSA_STATUS_INVALID_VALUE, "bytes is null");
+  const Problem pr{ratio, coff, head_dim, S, total_tokens, total_comp};
+  const csa_status_t st = check_problem(pr);
+  if (st) return st;
+  *bytes = make_plan(pr).ws_bwd;
+  return ok();
+}
+
+csa_status_t csa_compressor_fwd(const void* kv, const void* score, const float* ape, const int32_t* cu,
+                                int32_t S, int64_t total_tokens, int64_t total_comp, int32_t ratio,
+                                int32_t coff, int32_t head_dim, void* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  const Problem pr{ratio, coff, head_dim, S, total_tokens, total_comp};
+  csa_status_t st = check_problem(pr);
+  if (st) return st;
+  if (pr.N == 0) return ok();  // no output rows: nothing to do
+  if ((st = check_ptr(kv, "kv")) || (st = check_ptr(score, "score")) || (st = check_ptr(ape, "ape")) ||
+      (st = check_ptr(out, "out")))
+    return st;
+  if (!cu) return fail(CSA_STATUS_INVALID_VALUE, "cu_seqlens is null");
+  if (reinterpret_cast<uintptr_t>(cu) & 3u) return fail(CSA_STATUS_INVALID_VALUE, "cu_seqlens is not 4-byte aligned");
+  const Plan pl = make_plan(pr);
+  if (workspace_bytes < pl.ws_fwd)
+    return fail(CSA_STATUS_WORKSPACE_TOO_SMALL, "forward needs %llu workspace bytes, got %llu",
+                (unsigned long long)pl.ws_fwd, (unsigned long long)workspace_bytes);
+  if (pl.ws_fwd > 0 && (st = check_ptr(workspace, "workspace"))) return st;
+
+  if ((st = launch_scan_if_needed(pr, pl, cu, workspace, stream))) return st;
+  csa::FwdParams fp{};
+  fp.seg = seg_params(pr, pl, cu, workspace);
+  fp.kv = static_cast<const uint16_t*>(kv);
+  fp.score = static_cast<const uint16_t*>(score);
+  fp.ape = ape;
+  fp.out = static_cast<uint16_t*>(out);
+  fp.io_bytes = static_cast<uint32_t>(pr.T * pr.coff * pr.head_dim * 2);
+  fp.head_dim = head_dim;
+  fp.log2_chunks = pl.fwd_log2_chunks;
+  if (!csa::launch_fwd(ratio, coff, fp, pl.fwd, stream))
+    return fail(CSA_STATUS_NOT_SUPPORTED, "no forward kernel for this configuration");
+  return after_launch("forward");
+}
+
+csa_status_t csa_compressor_bwd_grads(const void* kv, const void* score, const float* ape, const int32_t* cu,
+                                      int32_t S, int64_t total_tokens, int64_t total_comp, int32_t ratio,
+                                      int32_t coff, int32_t head_dim, const void* dout, void* dkv, void* dscore,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const Problem pr{ratio, coff, head_dim, S, total_tokens, total_comp};
+  csa_status_t st = check_problem(pr);
+  if (st) return st;
+  const Plan pl = make_plan(pr);
+  if ((st = check_bwd_args(pr, pl, kv, score, ape, cu, dout, dkv, dscore, workspace, workspace_bytes))) return st;
+  return launch_bwd_grads(pr, pl, kv, score, ape, cu, dout, dkv, dscore, workspace, stream);
+}
+
+csa_status_t csa_compressor_bwd_dape_reduce(int32_t ratio, int32_t coff, int32_t head_dim, int32_t S,
+                                            int64_t total_tokens, int64_t total_comp, float* dape,
+                                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const Problem pr{ratio, coff, head_dim, S, total_tokens, total_comp};
+  csa_status_t st = check_problem(pr);
+  if (st) return st;
+  const Plan pl = make_plan(pr);
+  if ((st = check_ptr(dape, "dape"))) return st;
+  if (workspace_bytes < pl.ws_bwd)
+    return fail(CSA_STATUS_WORKSPACE_TOO_SMALL, "backward needs %llu workspace bytes, got %llu",
+                (unsigned long long)pl.ws_bwd, (unsigned long long)workspace_bytes);
+  if ((st = check_ptr(workspace, "workspace"))) return st;
+  return launch_reduce(pr, pl, dape, workspace, stream);
+}
+
+csa_status_t csa_compressor_bwd(const void* kv, const void* score, const float* ape, const int32_t* cu,
+                                int32_t S, int64_t total_tokens, int64_t total_comp, int32_t ratio, int32_t coff,
+                                int32_t head_dim, const void* dout, void* dkv, void* dscore, float* dape,
+                                int32_t deterministic, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  (void)deterministic;  // this build always reduces dAPE in a fixed order
+  const Problem pr{ratio, coff, head_dim, S, total_tokens, total_comp};
+  csa_status_t st = check_problem(pr);
+  if (st) return st;
+  const Plan pl = make_plan(pr);
+  if ((st = check_bwd_args(pr, pl, kv, score, ape, cu, dout, dkv, dscore, workspace, workspace_bytes))) return st;
+  if ((st = check_ptr(dape, "dape"))) return st;
+  if ((st = launch_bwd_grads(pr, pl, kv, score, ape, cu, dout, dkv, dscore, workspace, stream))) return st;
+  return launch_reduce(pr, pl, dape, workspace, stream);
+}
+
+}  // extern "C"

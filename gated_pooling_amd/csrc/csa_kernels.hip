@@ -1,0 +1,762 @@
+// csa_kernels.hip -- gfx950 kernels of the CSA/HCA Compressor (THD-packed
+// gated-softmax pooling), forward and backward.
+//
+// Sources (web pages): [PR5984] the NVIDIA/Megatron-LM pull request 5984
+// page (squashed cudnn-frontend #427 commit log); [PR710] the cudnn-frontend
+// pull request 710 page.
+//
+// Design (MI355X-first; the pages' kernels were written for another GPU and
+// only their semantics are kept):
+//   * The path is HBM-bound: per consumed kv/score slot it reads 4 bytes and
+//     does ~20 fp32 VALU operations, far from any contraction, so there is no
+//     MFMA.  Every consumed slot is read exactly once.
+//   * Work item = (output row n, chunk of C output columns).  A lane owns one
+//     chunk and walks output rows grid-stride; lanes of a wave take
+//     consecutive chunks, so each wave load covers contiguous bytes of one
+//     half-row (coalesced 16-byte loads for C = 8).
+//   * At coff = 2 a block's window is the previous block's first-half columns
+//     plus its own second-half columns ([PR5984: fused forward+backward
+//     commit]).  The lane loads exactly those 2*ratio half-row chunks, so no
+//     slot is loaded twice and no block-to-block hand-off is needed.
+//   * The window lives in VGPRs (ratio <= 4 keeps it to 2*4*C bf16 per
+//     tensor); APE for the lane's chunk is loaded once per lane.
+//   * Global memory goes through raw buffer instructions with exact byte
+//     ranges: an index mistake cannot fault, out-of-range loads read 0 and
+//     out-of-range stores are dropped.
+//   * Backward stores are disjoint and atomic-free: the lane that owns a
+//     window writes dkv/dscore for all of its slots; never-consumed slots get
+//     +0.0 from one owner each ([PR5984: zero-init folding commit]): the
+//     segment's last block writes its own first-half columns (coff = 2) and
+//     the segment's seqlen % ratio tail rows; extra "zero" workgroups write
+//     the rows of segments shorter than ratio and the rows past cu[S].
+//   * dAPE: per-lane fp32 accumulators, reduced in a fixed order inside the
+//     workgroup (butterfly shuffles, then waves in index order through LDS),
+//     one partial row per workgroup in the workspace, then a second kernel
+//     sums the partial rows in a fixed order.  Deterministic.
+//   * The cu_seqlens -> output-block offset scan runs in each workgroup's
+//     prologue (LDS) for up to kMaxLdsSegments segments; larger packs use a
+//     one-workgroup scan kernel writing the offsets to the workspace.
+//   * Floating point follows one fixed fp32 evaluation order (see
+//     include/csa.h); the library is compiled with -ffp-contract=off so only
+//     the explicit fmas below are fused.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "csa_launch.h"
+
+namespace csa {
+namespace {
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+// Word 3 of a gfx9 raw buffer descriptor: 32-bit data format, no swizzle.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kRsrcWord3);
+}
+
+// ---------------------------------------------------------------------------
+// C bf16 values of one row chunk, as C/2 packed dwords.
+// ---------------------------------------------------------------------------
+template <int C>
+struct Pack {
+  uint32_t w[C / 2];
+};
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int C>
+__device__ __forceinline__ Pack<C> load_pack(rsrc_t r, uint32_t byte_off) {
+  Pack<C> p;
+  if constexpr (C == 8) {
+    u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+    p.w[0] = v.x; p.w[1] = v.y; p.w[2] = v.z; p.w[3] = v.w;
+  } else if constexpr (C == 4) {
+    u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
+    p.w[0] = v.x; p.w[1] = v.y;
+  } else {
+    static_assert(C == 2, "C must be 2, 4 or 8");
+    p.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
+  }
+  return p;
+}
+
+template <int C>
+__device__ __forceinline__ void store_pack(rsrc_t r, uint32_t byte_off, const Pack<C>& p) {
+  if constexpr (C == 8) {
+    u32x4 v = {p.w[0], p.w[1], p.w[2], p.w[3]};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 0);
+  } else if constexpr (C == 4) {
+    u32x2 v = {p.w[0], p.w[1]};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(p.w[0], r, byte_off, 0, 0);
+  }
+}
+
+// C consecutive fp32 values (APE row chunk).
+template <int C>
+__device__ __forceinline__ void load_f32(rsrc_t r, uint32_t byte_off, float (&out)[C]) {
+  if constexpr (C == 8) {
+    u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+    u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off + 16, 0, 0);
+    out[0] = __uint_as_float(a.x); out[1] = __uint_as_float(a.y);
+    out[2] = __uint_as_float(a.z); out[3] = __uint_as_float(a.w);
+    out[4] = __uint_as_float(b.x); out[5] = __uint_as_float(b.y);
+    out[6] = __uint_as_float(b.z); out[7] = __uint_as_float(b.w);
+  } else if constexpr (C == 4) {
+    u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+    out[0] = __uint_as_float(a.x); out[1] = __uint_as_float(a.y);
+    out[2] = __uint_as_float(a.z); out[3] = __uint_as_float(a.w);
+  } else {
+    u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
+    out[0] = __uint_as_float(a.x); out[1] = __uint_as_float(a.y);
+  }
+}
+
+// bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits.
+template <int C>
+__device__ __forceinline__ float elem(const Pack<C>& p, int k) {
+  const uint32_t w = p.w[k >> 1];
+  return (k & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+}
+
+// Two fp32 -> bf16 with round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v.x = static_cast<__bf16>(lo);
+  v.y = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---------------------------------------------------------------------------
+// EXP: the fixed fp32 exponential of the evaluation order.
+//   y >= -104 (clamp; e^-104 is below half the smallest subnormal),
+//   k = rint(y log2 e), r = y - k ln2 in two fma steps (Cody-Waite with
+//   ln2 split as fp32(ln2) + fp32(ln2 - fp32(ln2))), e^r by its degree-6
+//   Taylor polynomial (Horner, coefficients fp32(1/n!)), scaled by 2^k.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float csa_exp(float y) {
+  constexpr float kLog2e = 1.44269504088896340736f;
+  constexpr float kLn2Hi = 0.693147180559945309417f;
+  constexpr float kLn2Lo = -1.904654299957768e-09f;  // ln 2 - fp32(ln 2)
+  y = fmaxf(y, -104.0f);
+  const float k = __builtin_rintf(y * kLog2e);
+  float r = __builtin_fmaf(-k, kLn2Hi, y);
+  r = __builtin_fmaf(-k, kLn2Lo, r);
+  float q = 1.0f / 720.0f;
+  q = __builtin_fmaf(q, r, 1.0f / 120.0f);
+  q = __builtin_fmaf(q, r, 1.0f / 24.0f);
+  q = __builtin_fmaf(q, r, 1.0f / 6.0f);
+  q = __builtin_fmaf(q, r, 0.5f);
+  q = __builtin_fmaf(q, r, 1.0f);
+  q = __builtin_fmaf(q, r, 1.0f);
+  return __builtin_ldexpf(q, static_cast<int>(k));
+}
+
+// One window, one column: weights e[], reciprocal R and the fp32 output o.
+template <int K>
+__device__ __forceinline__ float softmax_pool(const float (&x)[K], const float (&v)[K], float (&e)[K],
+                                              float& R) {
+  float m = x[0];
+#pragma unroll
+  for (int k = 1; k < K; ++k) m = fmaxf(m, x[k]);
+#pragma unroll
+  for (int k = 0; k < K; ++k) e[k] = csa_exp(x[k] - m);
+  float Z = e[0];
+#pragma unroll
+  for (int k = 1; k < K; ++k) Z = Z + e[k];
+  R = 1.0f / Z;
+  float acc = 0.0f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) acc = __builtin_fmaf(e[k], v[k], acc);
+  return acc * R;
+}
+
+// ---------------------------------------------------------------------------
+// Segment table: cu_seqlens and the exclusive scan of floor(L_s / ratio)
+// (output-block offsets), validated.  Small packs: built per workgroup in
+// LDS.  Large packs: read from the workspace (built by seg_scan_kernel).
+// ---------------------------------------------------------------------------
+struct SegTable {
+  const int32_t* cu;
+  const int32_t* off;
+};
+
+// Exclusive block-wide scan of int64 values; returns the block total.
+template <int NT>
+__device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t& excl, int64_t* s_wave) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int64_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) s_wave[wv] = incl;
+  __syncthreads();
+  int64_t before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int64_t t = s_wave[w];
+    before += (w < wv) ? t : 0;
+    total += t;
+  }
+  excl = before + incl - v;
+  __syncthreads();  // s_wave may be reused by the caller
+  return total;
+}
+
+// Returns true (uniformly across the block) iff cu is a valid pack for
+// (S, T_cap, N).  LDS layout: int64 scratch[NT/64], cu[S+1], off[S+1].
+template <int R, int NT>
+__device__ bool load_segment_table(const SegParams& sp, int32_t* lds, SegTable& t) {
+  if (sp.global_table) {
+    t.cu = sp.cu;
+    t.off = sp.g_off;
+    return __builtin_nontemporal_load(sp.g_flag) == 1;
+  }
+  const int S = sp.S;
+  int64_t* s_wave = reinterpret_cast<int64_t*>(lds);
+  int32_t* s_cu = lds + 2 * (NT / 64);
+  int32_t* s_off = s_cu + (S + 1);
+  const int tid = threadIdx.x;
+  for (int i = tid; i <= S; i += NT) s_cu[i] = sp.cu[i];
+  __syncthreads();
+  const int per = (S + NT - 1) / NT;
+  const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
+  int64_t local = 0;
+  int bad = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int32_t L = s_cu[s + 1] - s_cu[s];
+    bad |= (L < 0);
+    local += (L > 0) ? (L / R) : 0;
+  }
+  int64_t run;
+  const int64_t total = block_exclusive_scan<NT>(local, run, s_wave);
+  for (int s = s0; s < s1; ++s) {
+    s_off[s] = static_cast<int32_t>(run);
+    const int32_t L = s_cu[s + 1] - s_cu[s];
+    run += (L > 0) ? (L / R) : 0;
+  }
+  if (tid == 0) {
+    s_off[S] = static_cast<int32_t>(total);
+    bad |= (s_cu[0] != 0) | (static_cast<int64_t>(s_cu[S]) > sp.T_cap) | (total != sp.N);
+  }
+  t.cu = s_cu;
+  t.off = s_off;
+  return __syncthreads_or(bad) == 0;
+}
+
+// Largest s in [0, S) with off[s] <= n (requires n < off[S]); skips empty
+// segments because they share their offset with the next segment.
+__device__ __forceinline__ int find_segment(const int32_t* off, int S, int32_t n) {
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= n) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+template <int R, int CO, int C, int NT>
+__global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
+  extern __shared__ int32_t lds[];
+  SegTable tab;
+  if (!load_segment_table<R, NT>(p.seg, lds, tab)) return;
+
+  const uint32_t d = p.head_dim, W = CO * d;
+  const uint32_t lgG = p.log2_chunks, G = 1u << lgG;
+  const uint32_t L = blockIdx.x * NT + threadIdx.x;
+  const uint32_t g = L & (G - 1);
+  const uint32_t nstride = (gridDim.x * NT) >> lgG;
+  const uint32_t N = static_cast<uint32_t>(p.seg.N);
+  uint32_t n = L >> lgG;
+  if (n >= N) return;
+
+  const rsrc_t rkv = make_rsrc(p.kv, p.io_bytes);
+  const rsrc_t rsc = make_rsrc(p.score, p.io_bytes);
+  const rsrc_t rape = make_rsrc(p.ape, R * W * 4u);
+  const rsrc_t rout = make_rsrc(p.out, N * d * 2u);
+
+  // APE of this chunk: [half][position][column]
+  float ape_r[CO][R][C];
+#pragma unroll
+  for (int h = 0; h < CO; ++h)
+#pragma unroll
+    for (int i = 0; i < R; ++i) load_f32<C>(rape, (i * W + h * d + g * C) * 4u, ape_r[h][i]);
+
+  const uint32_t col_prev = g * C;                   // first half
+  const uint32_t col_own = (CO - 1) * d + g * C;     // second half at coff = 2
+  for (; n < N; n += nstride) {
+    const int s = find_segment(tab.off, p.seg.S, static_cast<int32_t>(n));
+    const uint32_t b = n - tab.off[s];
+    const uint32_t own = tab.cu[s] + b * R;
+    Pack<C> so[R], vo[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      so[i] = load_pack<C>(rsc, ((own + i) * W + col_own) * 2u);
+      vo[i] = load_pack<C>(rkv, ((own + i) * W + col_own) * 2u);
+    }
+    Pack<C> outp;
+    if (CO == 2 && b > 0) {
+      constexpr int K = CO * R;
+      Pack<C> sp[R], vp[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        sp[i] = load_pack<C>(rsc, ((own - R + i) * W + col_prev) * 2u);
+        vp[i] = load_pack<C>(rkv, ((own - R + i) * W + col_prev) * 2u);
+      }
+#pragma unroll
+      for (int kp = 0; kp < C / 2; ++kp) {
+        float o2[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int k = 2 * kp + hh;
+          float x[K], v[K], e[K], Rz;
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            x[i] = elem<C>(sp[i], k) + ape_r[0][i][k];
+            v[i] = elem<C>(vp[i], k);
+            x[R + i] = elem<C>(so[i], k) + ape_r[CO - 1][i][k];
+            v[R + i] = elem<C>(vo[i], k);
+          }
+          o2[hh] = softmax_pool<K>(x, v, e, Rz);
+        }
+        outp.w[kp] = pack_bf16x2(o2[0], o2[1]);
+      }
+    } else {
+#pragma unroll
+      for (int kp = 0; kp < C / 2; ++kp) {
+        float o2[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int k = 2 * kp + hh;
+          float x[R], v[R], e[R], Rz;
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            x[i] = elem<C>(so[i], k) + ape_r[CO - 1][i][k];
+            v[i] = elem<C>(vo[i], k);
+          }
+          o2[hh] = softmax_pool<R>(x, v, e, Rz);
+        }
+        outp.w[kp] = pack_bf16x2(o2[0], o2[1]);
+      }
+    }
+    store_pack<C>(rout, (n * d + g * C) * 2u, outp);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward: gradients, zero ownership, dAPE partials
+// ---------------------------------------------------------------------------
+
+// Zero a byte range [begin, end) of a buffer with 16-byte stores when both
+// ends are 16-byte aligned, 4-byte stores otherwise (rows are a multiple of
+// 4 bytes since coff * head_dim is even).
+__device__ __forceinline__ void zero_range(rsrc_t r, uint32_t begin, uint32_t end, uint32_t first,
+                                           uint32_t step) {
+  if (((begin | end) & 15u) == 0) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (uint32_t o = begin + first * 16u; o < end; o += step * 16u)
+      __builtin_amdgcn_raw_buffer_store_b128(z, r, o, 0, 0);
+  } else {
+    for (uint32_t o = begin + first * 4u; o < end; o += step * 4u)
+      __builtin_amdgcn_raw_buffer_store_b32(0u, r, o, 0, 0);
+  }
+}
+
+template <int R, int CO, int NT>
+__device__ void zero_sweep(const BwdParams& p, const SegTable& tab) {
+  const uint32_t W = CO * p.head_dim, row_bytes = W * 2u;
+  const rsrc_t rdkv = make_rsrc(p.dkv, p.io_bytes);
+  const rsrc_t rdsc = make_rsrc(p.dscore, p.io_bytes);
+  const uint32_t zid = blockIdx.x - p.main_wgs, nz = gridDim.x - p.main_wgs;
+  const int S = p.seg.S;
+  // rows of segments with no output block (L_s < ratio): whole rows
+  for (int s = zid; s < S; s += nz) {
+    if (tab.off[s + 1] == tab.off[s] && tab.cu[s + 1] > tab.cu[s]) {
+      const uint32_t b0 = tab.cu[s] * row_bytes, b1 = tab.cu[s + 1] * row_bytes;
+      zero_range(rdkv, b0, b1, threadIdx.x, NT);
+      zero_range(rdsc, b0, b1, threadIdx.x, NT);
+    }
+  }
+  // static-capacity padding rows past cu[S]
+  const uint32_t b0 = tab.cu[S] * row_bytes, b1 = static_cast<uint32_t>(p.seg.T_cap) * row_bytes;
+  zero_range(rdkv, b0, b1, zid * NT + threadIdx.x, nz * NT);
+  zero_range(rdsc, b0, b1, zid * NT + threadIdx.x, nz * NT);
+}
+
+template <int R, int CO, int C, int NT>
+__global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
+  extern __shared__ int32_t lds[];
+  SegTable tab;
+  const bool valid = load_segment_table<R, NT>(p.seg, lds, tab);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && !p.seg.global_table)
+    __builtin_nontemporal_store(valid ? 1 : 0, p.ws_flag);
+  if (!valid) return;
+  if (blockIdx.x >= p.main_wgs) {
+    zero_sweep<R, CO, NT>(p, tab);
+    return;
+  }
+
+  const uint32_t d = p.head_dim, W = CO * d;
+  const uint32_t lgG = p.log2_chunks, G = 1u << lgG;
+  const uint32_t L = blockIdx.x * NT + threadIdx.x;
+  const uint32_t g = L & (G - 1);
+  const uint32_t nstride = (p.main_wgs * NT) >> lgG;
+  const uint32_t N = static_cast<uint32_t>(p.seg.N);
+
+  const rsrc_t rkv = make_rsrc(p.kv, p.io_bytes);
+  const rsrc_t rsc = make_rsrc(p.score, p.io_bytes);
+  const rsrc_t rdkv = make_rsrc(p.dkv, p.io_bytes);
+  const rsrc_t rdsc = make_rsrc(p.dscore, p.io_bytes);
+  const rsrc_t rape = make_rsrc(p.ape, R * W * 4u);
+  const rsrc_t rdo = make_rsrc(p.dout, N * d * 2u);
+
+  float ape_r[CO][R][C];
+  float acc_r[CO][R][C];
+#pragma unroll
+  for (int h = 0; h < CO; ++h)
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      load_f32<C>(rape, (i * W + h * d + g * C) * 4u, ape_r[h][i]);
+#pragma unroll
+      for (int k = 0; k < C; ++k) acc_r[h][i][k] = 0.0f;
+    }
+
+  const uint32_t col_prev = g * C;
+  const uint32_t col_own = (CO - 1) * d + g * C;
+  for (uint32_t n = L >> lgG; n < N; n += nstride) {
+    const int s = find_segment(tab.off, p.seg.S, static_cast<int32_t>(n));
+    const uint32_t b = n - tab.off[s];
+    const uint32_t nb = tab.off[s + 1] - tab.off[s];
+    const uint32_t own = tab.cu[s] + b * R;
+    const Pack<C> gp = load_pack<C>(rdo, (n * d + g * C) * 2u);
+    Pack<C> so[R], vo[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      so[i] = load_pack<C>(rsc, ((own + i) * W + col_own) * 2u);
+      vo[i] = load_pack<C>(rkv, ((own + i) * W + col_own) * 2u);
+    }
+    if (CO == 2 && b > 0) {
+      constexpr int K = CO * R;
+      Pack<C> sp[R], vp[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        sp[i] = load_pack<C>(rsc, ((own - R + i) * W + col_prev) * 2u);
+        vp[i] = load_pack<C>(rkv, ((own - R + i) * W + col_prev) * 2u);
+      }
+      Pack<C> gkv[K], gsc[K];
+#pragma unroll
+      for (int kp = 0; kp < C / 2; ++kp) {
+        float a2[2][K], ds2[2][K];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int k = 2 * kp + hh;
+          float x[K], v[K], e[K], Rz;
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            x[i] = elem<C>(sp[i], k) + ape_r[0][i][k];
+            v[i] = elem<C>(vp[i], k);
+            x[R + i] = elem<C>(so[i], k) + ape_r[CO - 1][i][k];
+            v[R + i] = elem<C>(vo[i], k);
+          }
+          const float o = softmax_pool<K>(x, v, e, Rz);
+          const float Gk = Rz * elem<C>(gp, k);
+#pragma unroll
+          for (int i = 0; i < K; ++i) {
+            const float a = e[i] * Gk;
+            const float ds = a * (v[i] - o);
+            a2[hh][i] = a;
+            ds2[hh][i] = ds;
+          }
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            acc_r[0][i][k] += ds2[hh][i];
+            acc_r[CO - 1][i][k] += ds2[hh][R + i];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+          gkv[i].w[kp] = pack_bf16x2(a2[0][i], a2[1][i]);
+          gsc[i].w[kp] = pack_bf16x2(ds2[0][i], ds2[1][i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        store_pack<C>(rdkv, ((own - R + i) * W + col_prev) * 2u, gkv[i]);
+        store_pack<C>(rdsc, ((own - R + i) * W + col_prev) * 2u, gsc[i]);
+        store_pack<C>(rdkv, ((own + i) * W + col_own) * 2u, gkv[R + i]);
+        store_pack<C>(rdsc, ((own + i) * W + col_own) * 2u, gsc[R + i]);
+      }
+    } else {
+      Pack<C> gkv[R], gsc[R];
+#pragma unroll
+      for (int kp = 0; kp < C / 2; ++kp) {
+        float a2[2][R], ds2[2][R];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int k = 2 * kp + hh;
+          float x[R], v[R], e[R], Rz;
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            x[i] = elem<C>(so[i], k) + ape_r[CO - 1][i][k];
+            v[i] = elem<C>(vo[i], k);
+          }
+          const float o = softmax_pool<R>(x, v, e, Rz);
+          const float Gk = Rz * elem<C>(gp, k);
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            const float a = e[i] * Gk;
+            const float ds = a * (v[i] - o);
+            a2[hh][i] = a;
+            ds2[hh][i] = ds;
+            acc_r[CO - 1][i][k] += ds;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          gkv[i].w[kp] = pack_bf16x2(a2[0][i], a2[1][i]);
+          gsc[i].w[kp] = pack_bf16x2(ds2[0][i], ds2[1][i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        store_pack<C>(rdkv, ((own + i) * W + col_own) * 2u, gkv[i]);
+        store_pack<C>(rdsc, ((own + i) * W + col_own) * 2u, gsc[i]);
+      }
+    }
+    if (b + 1 == nb) {
+      // The segment's last block owns the never-read slots next to it.
+      Pack<C> z;
+#pragma unroll
+      for (int q = 0; q < C / 2; ++q) z.w[q] = 0u;
+      if (CO == 2) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          store_pack<C>(rdkv, ((own + i) * W + col_prev) * 2u, z);
+          store_pack<C>(rdsc, ((own + i) * W + col_prev) * 2u, z);
+        }
+      }
+      for (uint32_t t = own + R; t < static_cast<uint32_t>(tab.cu[s + 1]); ++t) {
+#pragma unroll
+        for (int h = 0; h < CO; ++h) {
+          store_pack<C>(rdkv, (t * W + h * d + g * C) * 2u, z);
+          store_pack<C>(rdsc, (t * W + h * d + g * C) * 2u, z);
+        }
+      }
+    }
+  }
+
+  // ---- dAPE: fixed-order reduction inside the workgroup ----
+  // 1) lanes of a wave that share a chunk (chunks < 64): xor butterfly.
+  if (G < 64) {
+    for (uint32_t o = G; o < 64; o <<= 1) {
+#pragma unroll
+      for (int h = 0; h < CO; ++h)
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+          for (int k = 0; k < C; ++k) acc_r[h][i][k] += __shfl_xor(acc_r[h][i][k], o, 64);
+    }
+  }
+  // 2) waves in index order into LDS red[h][i][c], c over the chunks this
+  //    workgroup covers (all G chunks when G <= NT, else a slice of NT).
+  const uint32_t wg_chunks = G < NT ? G : NT;
+  const uint32_t CW = wg_chunks * C;
+  float* red = reinterpret_cast<float*>(lds + p.lds_table_words);
+  for (uint32_t idx = threadIdx.x; idx < CO * R * CW; idx += NT) red[idx] = 0.0f;
+  __syncthreads();
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t gl = g & (wg_chunks - 1);
+  for (uint32_t w = 0; w < NT / 64; ++w) {
+    if (wave == w && (G >= 64 || lane < G)) {
+#pragma unroll
+      for (int h = 0; h < CO; ++h)
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+          for (int k = 0; k < C; ++k) red[(h * R + i) * CW + gl * C + k] += acc_r[h][i][k];
+    }
+    __syncthreads();
+  }
+  // 3) one partial row per (workgroup / slice): partial[row][i][h*d + col]
+  const uint32_t slices = G / wg_chunks;
+  const uint32_t prow = blockIdx.x / slices;
+  const uint32_t cbase = (blockIdx.x % slices) * CW;
+  const rsrc_t rpart = make_rsrc(p.partials, p.partial_rows * R * W * 4u);
+  for (uint32_t idx = threadIdx.x; idx < CO * R * CW; idx += NT) {
+    const uint32_t hi = idx / CW, c = idx - hi * CW;
+    const uint32_t h = hi / R, i = hi - h * R;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(red[idx]), rpart,
+                                          ((prow * R + i) * W + h * d + cbase + c) * 4u, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dAPE reduce: dape[j] = sum over partial rows, in a fixed order.
+// Workgroup = 16 waves x 64 columns; wave w sums rows w, w+16, ... in order;
+// then lane-column totals are added wave 0..15 in order.
+// ---------------------------------------------------------------------------
+constexpr int kReduceNT = 1024;
+
+__global__ __launch_bounds__(kReduceNT) void dape_reduce_kernel(ReduceParams p) {
+  __shared__ float part[kReduceNT / 64][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t col = blockIdx.x * 64 + lane;
+  const uint32_t cols = p.cols;
+  const bool valid = __builtin_nontemporal_load(p.ws_flag) == 1;
+  if (!valid) return;  // bad cu_seqlens: leave dape untouched
+  const rsrc_t rpart = make_rsrc(p.partials, p.rows * cols * 4u);
+  float s = 0.0f;
+  if (col < cols) {
+    uint32_t r = wave;
+    // a few independent loads in flight per lane, summed in row order
+    for (; r + 3 * (kReduceNT / 64) < p.rows; r += 4 * (kReduceNT / 64)) {
+      float v0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpart, (r * cols + col) * 4u, 0, 0));
+      float v1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpart, ((r + 16) * cols + col) * 4u, 0, 0));
+      float v2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpart, ((r + 32) * cols + col) * 4u, 0, 0));
+      float v3 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpart, ((r + 48) * cols + col) * 4u, 0, 0));
+      s = s + v0;
+      s = s + v1;
+      s = s + v2;
+      s = s + v3;
+    }
+    for (; r < p.rows; r += kReduceNT / 64)
+      s = s + __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpart, (r * cols + col) * 4u, 0, 0));
+  }
+  part[wave][lane] = s;
+  __syncthreads();
+  if (wave == 0 && col < cols) {
+    float t = part[0][lane];
+#pragma unroll
+    for (int w = 1; w < kReduceNT / 64; ++w) t = t + part[w][lane];
+    p.dape[col] = t;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Offset scan for packs with more than kMaxLdsSegments segments: one
+// workgroup walks cu in chunks, writes off[0..S] and a validity flag.
+// ---------------------------------------------------------------------------
+constexpr int kScanNT = 1024;
+
+template <int R>
+__global__ __launch_bounds__(kScanNT) void seg_scan_kernel(SegParams sp, int32_t* off, int32_t* flag) {
+  __shared__ int64_t s_wave[kScanNT / 64];
+  __shared__ int s_bad;
+  const int S = sp.S, tid = threadIdx.x;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  int64_t carry = 0;
+  for (int base = 0; base < S; base += kScanNT) {
+    const int s = base + tid;
+    int64_t nb = 0;
+    if (s < S) {
+      const int32_t L = sp.cu[s + 1] - sp.cu[s];
+      if (L < 0) s_bad = 1;
+      nb = (L > 0) ? (L / R) : 0;
+    }
+    int64_t excl;
+    const int64_t total = block_exclusive_scan<kScanNT>(nb, excl, s_wave);
+    if (s < S) off[s] = static_cast<int32_t>(carry + excl);
+    carry += total;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    off[S] = static_cast<int32_t>(carry);
+    const bool bad = s_bad || sp.cu[0] != 0 || static_cast<int64_t>(sp.cu[S]) > sp.T_cap || carry != sp.N;
+    *flag = bad ? 0 : 1;
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <int R, int CO, int C>
+static void launch_fwd_rcc(const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
+  hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads>), dim3(sh.grid), dim3(kFwdThreads), sh.lds_bytes, st, p);
+}
+
+template <int R, int CO, int C, int NT>
+static void launch_bwd_rccn(const BwdParams& p, const LaunchShape& sh, hipStream_t st) {
+  hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT>), dim3(sh.grid), dim3(NT), sh.lds_bytes, st, p);
+}
+
+template <int R, int CO>
+static bool launch_fwd_rc(const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
+  switch (sh.cols) {
+    case 8: launch_fwd_rcc<R, CO, 8>(p, sh, st); return true;
+    case 4: launch_fwd_rcc<R, CO, 4>(p, sh, st); return true;
+    case 2: launch_fwd_rcc<R, CO, 2>(p, sh, st); return true;
+  }
+  return false;
+}
+
+template <int R, int CO, int C>
+static bool launch_bwd_rcc(const BwdParams& p, const LaunchShape& sh, hipStream_t st) {
+  switch (sh.threads) {
+    case 256: launch_bwd_rccn<R, CO, C, 256>(p, sh, st); return true;
+    case 512: launch_bwd_rccn<R, CO, C, 512>(p, sh, st); return true;
+    case 1024: launch_bwd_rccn<R, CO, C, 1024>(p, sh, st); return true;
+  }
+  return false;
+}
+
+template <int R, int CO>
+static bool launch_bwd_rc(const BwdParams& p, const LaunchShape& sh, hipStream_t st) {
+  switch (sh.cols) {
+    case 8: return launch_bwd_rcc<R, CO, 8>(p, sh, st);
+    case 4: return launch_bwd_rcc<R, CO, 4>(p, sh, st);
+    case 2: return launch_bwd_rcc<R, CO, 2>(p, sh, st);
+  }
+  return false;
+}
+
+bool launch_fwd(int ratio, int coff, const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
+  if (ratio == 4 && coff == 2) return launch_fwd_rc<4, 2>(p, sh, st);
+  if (ratio == 4 && coff == 1) return launch_fwd_rc<4, 1>(p, sh, st);
+  if (ratio == 2 && coff == 2) return launch_fwd_rc<2, 2>(p, sh, st);
+  if (ratio == 2 && coff == 1) return launch_fwd_rc<2, 1>(p, sh, st);
+  return false;
+}
+
+bool launch_bwd(int ratio, int coff, const BwdParams& p, const LaunchShape& sh, hipStream_t st) {
+  if (ratio == 4 && coff == 2) return launch_bwd_rc<4, 2>(p, sh, st);
+  if (ratio == 4 && coff == 1) return launch_bwd_rc<4, 1>(p, sh, st);
+  if (ratio == 2 && coff == 2) return launch_bwd_rc<2, 2>(p, sh, st);
+  if (ratio == 2 && coff == 1) return launch_bwd_rc<2, 1>(p, sh, st);
+  return false;
+}
+
+void launch_dape_reduce(const ReduceParams& p, hipStream_t st) {
+  const uint32_t grid = (p.cols + 63) / 64;
+  hipLaunchKernelGGL(dape_reduce_kernel, dim3(grid), dim3(kReduceNT), 0, st, p);
+}
+
+bool launch_seg_scan(int ratio, const SegParams& sp, int32_t* off, int32_t* flag, hipStream_t st) {
+  if (ratio == 4) {
+    hipLaunchKernelGGL(seg_scan_kernel<4>, dim3(1), dim3(kScanNT), 0, st, sp, off, flag);
+    return true;
+  }
+  if (ratio == 2) {
+    hipLaunchKernelGGL(seg_scan_kernel<2>, dim3(1), dim3(kScanNT), 0, st, sp, off, flag);
+    return true;
+  }
+  return false;
+}
+
+}  // namespace csa

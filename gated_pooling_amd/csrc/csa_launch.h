@@ -1,0 +1,75 @@
+// csa_launch.h -- internal interface between the C ABI (csa_api.cpp) and the
+// gfx950 kernels (csa_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+constexpr int kFwdThreads = 256;
+// Packs with more segments than this build their offset table with a
+// separate scan kernel into the workspace instead of in each workgroup's LDS.
+constexpr int kMaxLdsSegments = 2048;
+
+struct SegParams {
+  const int32_t* cu;      // device cu_seqlens [S + 1]
+  const int32_t* g_off;   // offsets in the workspace (large packs) or null
+  const int32_t* g_flag;  // validity flag in the workspace (large packs) or null
+  int64_t T_cap;          // total_tokens (row capacity)
+  int64_t N;              // total_comp as given by the caller
+  int32_t S;
+  int32_t global_table;   // 1: use g_off / g_flag
+};
+
+struct FwdParams {
+  SegParams seg;
+  const uint16_t* kv;
+  const uint16_t* score;
+  const float* ape;
+  uint16_t* out;
+  uint32_t io_bytes;      // total_tokens * coff * head_dim * 2
+  uint32_t head_dim;
+  uint32_t log2_chunks;   // log2(head_dim / cols)
+};
+
+struct BwdParams {
+  SegParams seg;
+  const uint16_t* kv;
+  const uint16_t* score;
+  const float* ape;
+  const uint16_t* dout;
+  uint16_t* dkv;
+  uint16_t* dscore;
+  float* partials;        // [partial_rows, ratio, coff * head_dim] in the workspace
+  int32_t* ws_flag;       // validity flag in the workspace
+  uint32_t io_bytes;
+  uint32_t head_dim;
+  uint32_t log2_chunks;
+  uint32_t main_wgs;      // workgroups [0, main_wgs) compute windows, the rest zero-fill
+  uint32_t partial_rows;
+  uint32_t lds_table_words;
+};
+
+struct ReduceParams {
+  const float* partials;
+  float* dape;
+  const int32_t* ws_flag;
+  uint32_t rows;
+  uint32_t cols;          // ratio * coff * head_dim
+};
+
+struct LaunchShape {
+  uint32_t grid;
+  uint32_t threads;
+  uint32_t cols;          // output columns per lane (2, 4 or 8)
+  size_t lds_bytes;
+};
+
+bool launch_fwd(int ratio, int coff, const FwdParams& p, const LaunchShape& sh, hipStream_t st);
+bool launch_bwd(int ratio, int coff, const BwdParams& p, const LaunchShape& sh, hipStream_t st);
+void launch_dape_reduce(const ReduceParams& p, hipStream_t st);
+bool launch_seg_scan(int ratio, const SegParams& sp, int32_t* off, int32_t* flag, hipStream_t st);
+
+}  // namespace csa

@@ -65,6 +65,8 @@ def lib():
         L.oracle_bf16_from_f32.argtypes = [ctypes.c_float]
         L.oracle_f32_from_bf16.restype = ctypes.c_float
         L.oracle_f32_from_bf16.argtypes = [ctypes.c_uint16]
+        L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_num_threads.argtypes = []
         L.oracle_total_comp.restype = ctypes.c_int
         L.oracle_total_comp.argtypes = [P, i32, i32, P]
         L.oracle_fwd_f32.restype = ctypes.c_int
@@ -90,6 +92,11 @@ def _c(a, dtype):
 def _check(rc: int, what: str):
     if rc != 0:
         raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().oracle_num_threads())
 
 
 def total_comp(cu, r: int) -> int:
@@ -130,28 +137,33 @@ def f64_from_bits(bits) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
-def fwd_f32(kv, score, ape, cu, T_cap: int, r: int, c: int, d: int) -> np.ndarray:
+def fwd_f32(kv, score, ape, cu, T_cap: int, r: int, c: int, d: int, out=None) -> np.ndarray:
     kv, score = _c(kv, np.uint16), _c(score, np.uint16)
     ape, cu = _c(ape, np.float32), _c(cu, np.int32)
     N = total_comp(cu, r)
-    out = np.full((N, d), 0x7FC0, np.uint16)
+    if out is None:
+        out = np.full((N, d), 0x7FC0, np.uint16)
     _check(lib().oracle_fwd_f32(_ptr(kv), _ptr(score), _ptr(ape), _ptr(cu), len(cu) - 1,
                                 T_cap, r, c, d, _ptr(out), N), "fwd_f32")
     return out
 
 
-def bwd_f32(kv, score, ape, cu, T_cap: int, r: int, c: int, d: int, dout):
-    """Returns (dkv bits, dscore bits, dape f64, ds32 f32, o32 f32)."""
+def bwd_outputs(T_cap: int, r: int, c: int, d: int, N: int):
+    """NaN-prefilled output arrays for bwd_f32 (a slot the oracle forgot to
+    write stays visible).  Reusable across calls of the same shape."""
+    W = c * d
+    return (np.full((T_cap, W), 0x7FC0, np.uint16), np.full((T_cap, W), 0x7FC0, np.uint16),
+            np.full((r, W), np.nan, np.float64), np.full((T_cap, W), np.nan, np.float32),
+            np.full((N, d), np.nan, np.float32))
+
+
+def bwd_f32(kv, score, ape, cu, T_cap: int, r: int, c: int, d: int, dout, outs=None):
+    """Returns (dkv bits, dscore bits, dape f64, ds32 f32, o32 f32).  `outs`
+    may pass arrays from bwd_outputs() to avoid reallocating."""
     kv, score = _c(kv, np.uint16), _c(score, np.uint16)
     ape, cu, dout = _c(ape, np.float32), _c(cu, np.int32), _c(dout, np.uint16)
     N = total_comp(cu, r)
-    W = c * d
-    # NaN prefill: any slot the oracle forgot to write stays visible
-    dkv = np.full((T_cap, W), 0x7FC0, np.uint16)
-    dscore = np.full((T_cap, W), 0x7FC0, np.uint16)
-    dape = np.full((r, W), np.nan, np.float64)
-    ds32 = np.full((T_cap, W), np.nan, np.float32)
-    o32 = np.full((N, d), np.nan, np.float32)
+    dkv, dscore, dape, ds32, o32 = outs if outs is not None else bwd_outputs(T_cap, r, c, d, N)
     _check(lib().oracle_bwd_f32(_ptr(kv), _ptr(score), _ptr(ape), _ptr(cu), len(cu) - 1,
                                 T_cap, r, c, d, _ptr(dout), N, _ptr(dkv), _ptr(dscore),
                                 _ptr(dape), _ptr(ds32), _ptr(o32)), "bwd_f32")

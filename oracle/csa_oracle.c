@@ -72,6 +72,7 @@
  * sum_k ds_k = 0 per window; f32 vs f64 agreement within bf16 rounding.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -146,6 +147,9 @@ void oracle_exp_constants(float* out)
     out[3] = EXP_Y_MIN;
     for (int n = 0; n < 7; ++n) out[4 + n] = EXP_C[n];
 }
+
+/* OpenMP threads used by the parallel window loops (reported with timings). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------------- */
 /* Pack bookkeeping                                                        */

@@ -120,3 +120,26 @@ def random_pack(rng, max_segments=5, max_len=40, max_pad=7):
         cu.append(cu[-1] + L)
     T = cu[-1] + int(rng.integers(0, max_pad + 1))
     return cu, T
+
+
+def consumed_mask(cu, T, r, coff, d):
+    """Vectorised slot-side membership: bool [T, coff*d], True where some
+    window reads the slot (same rules as `consumer`)."""
+    cu = np.asarray(cu, np.int64)
+    S = len(cu) - 1
+    W = coff * d
+    t = np.arange(T, dtype=np.int64)
+    s = np.searchsorted(cu, t, side="right") - 1
+    inside = (s >= 0) & (s < S) & (t < cu[-1])
+    s = np.clip(s, 0, max(S - 1, 0))
+    u = t - cu[s] if S else np.zeros_like(t)
+    blk = u // r
+    nb = (cu[s + 1] - cu[s]) // r if S else np.zeros_like(t)
+    in_block = inside & (blk < nb)
+    mask = np.zeros((T, W), bool)
+    if coff == 1:
+        mask[in_block, :] = True
+    else:
+        mask[in_block, d:] = True
+        mask[in_block & (blk + 1 < nb), :d] = True
+    return mask

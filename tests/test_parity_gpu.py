@@ -1,0 +1,263 @@
+"""GPU parity: libcsa (HIP, through the C ABI) against the CPU oracle.
+
+Contract (checked element by element on seeded inputs):
+  * out, dKV, dScore: bit-identical to the oracle's fp32 evaluation order
+    (the stated tolerance is 1 bf16 ulp; both sides evaluate the same fixed
+    fp32 order, so the expected difference is none);
+  * never-consumed dKV/dScore slots: exactly 0x0000 although the output
+    buffers were filled with NaN before the call;
+  * dAPE: |gpu - ref| <= 1e-5 * max(|ref|, max|ref|) with ref the double sum
+    of the oracle's fp32 ds values;
+  * repeated runs are bit-identical (dAPE included).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gated_pooling_amd as G
+import oracle
+from gated_pooling_amd import inputs
+from tests import brute
+
+pytestmark = pytest.mark.gpu
+
+NAN_BF16 = 0x7FC0
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    G.lib()  # fail loudly if the HIP library is missing
+    return torch.device("cuda:0")
+
+
+def bf16_nan(shape, device):
+    return torch.full(shape, NAN_BF16, dtype=torch.int16, device=device).view(torch.bfloat16)
+
+
+def run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N, stages=False):
+    """Forward and backward on the GPU with NaN-prefilled outputs; returns
+    numpy (out bits, dkv bits, dscore bits, dape f32)."""
+    W = c * d
+    cu_d = torch.tensor(cu, dtype=torch.int32, device=dev)
+    kv_d, sc_d, ape_d, dout_d = kv.to(dev), sc.to(dev), ape.to(dev), dout.to(dev)
+    out = bf16_nan((N, d), dev)
+    G.compressor_fwd(kv_d, sc_d, ape_d, cu_d, r, c, N, out=out)
+    dkv, dsc = bf16_nan((T, W), dev), bf16_nan((T, W), dev)
+    dape = torch.full((r, W), float("nan"), dtype=torch.float32, device=dev)
+    if stages:
+        nbytes = G.csa_compressor_bwd_workspace_size(r, c, d, len(cu) - 1, T, N)
+        ws = G.workspace(nbytes, dev)
+        P = lambda t: t.data_ptr()  # noqa: E731
+        s = torch.cuda.current_stream().cuda_stream
+        G.csa_compressor_bwd_grads(P(kv_d), P(sc_d), P(ape_d), P(cu_d), len(cu) - 1, T, N, r, c, d, P(dout_d),
+                                   P(dkv), P(dsc), P(ws), ws.numel(), s)
+        G.csa_compressor_bwd_dape_reduce(r, c, d, len(cu) - 1, T, N, P(dape), P(ws), ws.numel(), s)
+    else:
+        G.compressor_bwd(kv_d, sc_d, ape_d, cu_d, r, c, N, dout_d, dkv=dkv, dscore=dsc, dape=dape)
+    torch.cuda.synchronize()
+    return (inputs.bits(out.cpu()), inputs.bits(dkv.cpu()), inputs.bits(dsc.cpu()), dape.cpu().numpy())
+
+
+def ordered(b):
+    b = np.asarray(b).astype(np.int32)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def assert_bits_equal(got, ref, name):
+    diff = got != ref
+    n = int(np.count_nonzero(diff))
+    if n:
+        idx = np.argwhere(diff)[:5].tolist()
+        dist = np.abs(ordered(got) - ordered(ref))
+        raise AssertionError(f"{name}: {n}/{got.size} elements differ (max ordered distance "
+                             f"{int(dist.max())}; first at {idx}: got {got[diff][:5]} ref {ref[diff][:5]})")
+
+
+def assert_dape(got, ref):
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    err = np.abs(got.astype(np.float64) - ref)
+    tol = 1e-5 * np.maximum(np.abs(ref), scale)
+    assert np.all(err <= tol), f"dAPE max err {err.max():.3e}, max rel-to-scale {(err / scale).max():.3e}"
+
+
+def check_against_oracle(cu, T, r, c, d, kv, sc, ape, dout, got):
+    N = oracle.total_comp(cu, r)
+    kvb, scb, apen, doutb = inputs.bits(kv), inputs.bits(sc), ape.numpy(), inputs.bits(dout)
+    out_ref = oracle.fwd_f32(kvb, scb, apen, cu, T, r, c, d)
+    dkv_ref, dsc_ref, dape_ref, _, _ = oracle.bwd_f32(kvb, scb, apen, cu, T, r, c, d, doutb)
+    out, dkv, dsc, dape = got
+    assert out.shape == (N, d)
+    assert_bits_equal(out, out_ref, "out")
+    assert_bits_equal(dkv, dkv_ref, "dkv")
+    assert_bits_equal(dsc, dsc_ref, "dscore")
+    assert_dape(dape, dape_ref)
+    # zero ownership: every never-consumed slot is +0.0 exactly
+    unused = ~brute.consumed_mask(cu, T, r, c, d)
+    assert np.all(dkv[unused] == 0) and np.all(dsc[unused] == 0)
+    return out_ref, dkv_ref, dsc_ref, dape_ref
+
+
+# ---------------------------------------------------------------------------
+# every workload at its full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_workload_parity(dev, name):
+    wl = inputs.WORKLOADS[name]
+    cu, T, r, c, d = list(wl.cu_seqlens), wl.total_tokens, wl.ratio, wl.coff, wl.head_dim
+    N = G.csa_compressor_total_comp(cu, r)
+    assert N == oracle.total_comp(cu, r)
+    kv, sc, ape, dout = inputs.make_tensors(wl, N)
+    got = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N)
+    check_against_oracle(cu, T, r, c, d, kv, sc, ape, dout, got)
+
+
+def test_stage_split_equals_full_backward(dev):
+    wl = inputs.WORKLOADS["ragged_d128_r4_c2"]
+    cu, T, r, c, d = list(wl.cu_seqlens), wl.total_tokens, wl.ratio, wl.coff, wl.head_dim
+    N = G.csa_compressor_total_comp(cu, r)
+    kv, sc, ape, dout = inputs.make_tensors(wl, N)
+    a = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N)
+    b = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N, stages=True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("name", ["3x8192_d512_r4_c2", "ragged_d128_r4_c1", "ragged_d128_r4_c2",
+                                  "1x8192_d128_r2_c2"])
+def test_repeat_runs_bit_identical(dev, name):
+    wl = inputs.WORKLOADS[name]
+    cu, T, r, c, d = list(wl.cu_seqlens), wl.total_tokens, wl.ratio, wl.coff, wl.head_dim
+    N = G.csa_compressor_total_comp(cu, r)
+    kv, sc, ape, dout = inputs.make_tensors(wl, N)
+    first = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N)
+    for _ in range(4):
+        again = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N)
+        for x, y in zip(first, again):
+            assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+# ---------------------------------------------------------------------------
+# never-read inputs cannot leak; degenerate packs
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny_r4_c2_d16", "ragged_d128_r4_c1", "ragged_d128_r4_c2"])
+def test_poisoned_unread_inputs_do_not_leak(dev, name):
+    """NaN in every kv/score slot no window reads (tails, short segments,
+    last-block first halves, padding) changes nothing."""
+    wl = inputs.WORKLOADS[name]
+    cu, T, r, c, d = list(wl.cu_seqlens), wl.total_tokens, wl.ratio, wl.coff, wl.head_dim
+    N = G.csa_compressor_total_comp(cu, r)
+    kv, sc, ape, dout = inputs.make_tensors(wl, N)
+    unused = torch.from_numpy(~brute.consumed_mask(cu, T, r, c, d))
+    assert int(unused.sum()) > 0
+    kvp, scp = kv.clone(), sc.clone()
+    kvp[unused] = float("nan")
+    scp[unused] = float("nan")
+    got = run_gpu(dev, cu, T, r, c, d, kvp, scp, ape, dout, N)
+    check_against_oracle(cu, T, r, c, d, kv, sc, ape, dout, got)
+
+
+@pytest.mark.parametrize("cu,T,r,c,d", [
+    ([0, 1, 4, 6, 9], 16, 4, 2, 16),      # every segment shorter than ratio, padding
+    ([0, 1, 2, 3], 3, 4, 1, 128),         # no padding, no blocks
+    ([0, 1, 1, 2], 8, 2, 2, 8),           # 1-token segments at ratio 2
+    ([0], 32, 4, 2, 16),                  # no segments at all: all padding
+    ([0, 0, 0], 0, 4, 2, 16),             # empty pack
+])
+def test_no_output_rows(dev, cu, T, r, c, d):
+    """total_comp == 0: the forward does nothing, the backward still writes
+    +0.0 everywhere and dAPE = 0."""
+    N = G.csa_compressor_total_comp(cu, r)
+    assert N == 0
+    wl = inputs.custom("deg", np.diff(cu).tolist(), T, r, c, d)
+    kv, sc, ape, dout = inputs.make_tensors(wl, N)
+    out, dkv, dsc, dape = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N)
+    assert out.shape == (0, d)
+    assert np.all(dkv == 0) and np.all(dsc == 0)
+    assert np.all(dape.view(np.uint32) == 0)
+
+
+def test_many_segments_use_workspace_table(dev):
+    """More segments than fit the per-workgroup LDS table (the offset scan
+    then runs as its own kernel): 5000 short segments of 0..13 tokens."""
+    rng = np.random.default_rng(21)
+    lengths = rng.integers(0, 14, size=5000).tolist()
+    T = int(sum(lengths)) + 37
+    for c in (1, 2):
+        wl = inputs.custom("many", lengths, T, 4, c, 16, seed=5)
+        cu = list(wl.cu_seqlens)
+        N = G.csa_compressor_total_comp(cu, 4)
+        assert G.csa_compressor_fwd_workspace_size(4, c, 16, 5000, T, N) > 0
+        kv, sc, ape, dout = inputs.make_tensors(wl, N)
+        got = run_gpu(dev, cu, T, 4, c, 16, kv, sc, ape, dout, N)
+        check_against_oracle(cu, T, 4, c, 16, kv, sc, ape, dout, got)
+
+
+def _random_cases(n=24, seed=77):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        S = int(rng.integers(1, 9))
+        lengths = rng.integers(0, 300, size=S).tolist()
+        T = int(sum(lengths)) + int(rng.integers(0, 20))
+        r = int(rng.choice([2, 4]))
+        c = int(rng.choice([1, 2]))
+        d = int(rng.choice([2, 4, 8, 16, 32, 64, 256, 1024]))
+        if T == 0:
+            T = 1
+        cases.append((lengths, T, r, c, d, 100 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases())
+def test_random_small_packs(dev, case):
+    """Ragged packs over head_dim 2..1024 (every lane layout: fewer columns
+    than a lane holds, chunks per row below and above a wave and a
+    workgroup)."""
+    lengths, T, r, c, d, seed = case
+    wl = inputs.custom("rand", lengths, T, r, c, d, seed=seed)
+    cu = list(wl.cu_seqlens)
+    N = G.csa_compressor_total_comp(cu, r)
+    kv, sc, ape, dout = inputs.make_tensors(wl, N)
+    got = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N)
+    check_against_oracle(cu, T, r, c, d, kv, sc, ape, dout, got)
+
+
+def test_extreme_scores_and_subnormals(dev):
+    """Score spreads that push EXP to its clamp and products into fp32
+    subnormals: still bit-identical (IEEE subnormals on both sides)."""
+    wl = inputs.custom("extreme", [64, 40, 7], 128, 4, 2, 64, seed=9)
+    cu = list(wl.cu_seqlens)
+    N = G.csa_compressor_total_comp(cu, 4)
+    kv, sc, ape, dout = inputs.make_tensors(wl, N)
+    g = torch.Generator().manual_seed(4)
+    sc = (sc.float() * torch.where(torch.rand(sc.shape, generator=g) < 0.3, 60.0, 1.0)).to(torch.bfloat16)
+    dout = (dout.float() * 1e-36).to(torch.bfloat16)
+    got = run_gpu(dev, cu, 128, 4, 2, 64, kv, sc, ape, dout, N)
+    check_against_oracle(cu, 128, 4, 2, 64, kv, sc, ape, dout, got)
+
+
+def test_invalid_device_cu_seqlens_touches_nothing(dev):
+    """cu_seqlens that contradicts total_comp (caller error, only detectable
+    on the device): the kernels leave every output as it was."""
+    cu_true = [0, 37, 64]
+    N = 15
+    wl = inputs.custom("bad", [37, 27], 64, 4, 2, 16)
+    kv, sc, ape, dout = inputs.make_tensors(wl, N)
+    bad = torch.tensor([0, 37, 60], dtype=torch.int32, device=dev)  # implies 9 + 5 = 14 blocks
+    out = bf16_nan((N, 16), dev)
+    G.compressor_fwd(kv.to(dev), sc.to(dev), ape.to(dev), bad, 4, 2, N, out=out)
+    dkv, dsc = bf16_nan((64, 32), dev), bf16_nan((64, 32), dev)
+    dape = torch.full((4, 32), float("nan"), device=dev)
+    G.compressor_bwd(kv.to(dev), sc.to(dev), ape.to(dev), bad, 4, 2, N, dout.to(dev), dkv=dkv, dscore=dsc, dape=dape)
+    torch.cuda.synchronize()
+    assert np.all(inputs.bits(out.cpu()) == NAN_BF16)
+    assert np.all(inputs.bits(dkv.cpu()) == NAN_BF16)
+    assert torch.isnan(dape.cpu()).all()
+    del cu_true
