@@ -606,42 +606,40 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // dAPE reduce: dape[j] = sum over partial rows, in a fixed order.
-// Workgroup = 16 waves x 64 columns; wave w sums rows w, w+16, ... in order;
-// then lane-column totals are added wave 0..15 in order.
+// Workgroup = 16 waves x 64 columns; wave w sums rows w, w+16, w+32, ... in
+// increasing order (loads issued 16 at a time so the whole column slice is
+// in flight at once), then the 16 wave totals are added in wave order.
 // ---------------------------------------------------------------------------
 constexpr int kReduceNT = 1024;
+constexpr int kReduceWaves = kReduceNT / 64;
+constexpr int kReduceBatch = 16;
 
 __global__ __launch_bounds__(kReduceNT) void dape_reduce_kernel(ReduceParams p) {
-  __shared__ float part[kReduceNT / 64][64];
+  __shared__ float part[kReduceWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t col = blockIdx.x * 64 + lane;
-  const uint32_t cols = p.cols;
-  const bool valid = __builtin_nontemporal_load(p.ws_flag) == 1;
-  if (!valid) return;  // bad cu_seqlens: leave dape untouched
-  const rsrc_t rpart = make_rsrc(p.partials, p.rows * cols * 4u);
+  const uint32_t cols = p.cols, rows = p.rows;
+  if (__builtin_nontemporal_load(p.ws_flag) != 1) return;  // bad cu_seqlens: leave dape untouched
+  const rsrc_t rpart = make_rsrc(p.partials, rows * cols * 4u);
   float s = 0.0f;
   if (col < cols) {
-    uint32_t r = wave;
-    // a few independent loads in flight per lane, summed in row order
-    for (; r + 3 * (kReduceNT / 64) < p.rows; r += 4 * (kReduceNT / 64)) {
-      float v0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpart, (r * cols + col) * 4u, 0, 0));
-      float v1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpart, ((r + 16) * cols + col) * 4u, 0, 0));
-      float v2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpart, ((r + 32) * cols + col) * 4u, 0, 0));
-      float v3 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpart, ((r + 48) * cols + col) * 4u, 0, 0));
-      s = s + v0;
-      s = s + v1;
-      s = s + v2;
-      s = s + v3;
+    for (uint32_t base = wave; base < rows; base += kReduceWaves * kReduceBatch) {
+      float v[kReduceBatch];
+#pragma unroll
+      for (int u = 0; u < kReduceBatch; ++u)
+        v[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rpart, ((base + u * kReduceWaves) * cols + col) * 4u, 0, 0));
+#pragma unroll
+      for (int u = 0; u < kReduceBatch; ++u)
+        if (base + u * kReduceWaves < rows) s = s + v[u];
     }
-    for (; r < p.rows; r += kReduceNT / 64)
-      s = s + __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpart, (r * cols + col) * 4u, 0, 0));
   }
   part[wave][lane] = s;
   __syncthreads();
   if (wave == 0 && col < cols) {
     float t = part[0][lane];
 #pragma unroll
-    for (int w = 1; w < kReduceNT / 64; ++w) t = t + part[w][lane];
+    for (int w = 1; w < kReduceWaves; ++w) t = t + part[w][lane];
     p.dape[col] = t;
   }
 }
