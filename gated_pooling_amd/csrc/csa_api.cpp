@@ -16,9 +16,9 @@
 //
 // Tuning knobs (environment, read once per process; every value is
 // validated and falls back to the default):
-//   CSA_FWD_COLS      output columns per lane in the forward (2, 4, 8)
+//   CSA_FWD_COLS      output columns per lane in the forward (2, 4)
 //   CSA_FWD_MAX_WGS   forward grid cap in workgroups of 256 threads
-//   CSA_BWD_COLS      output columns per lane in the backward (2, 4, 8)
+//   CSA_BWD_COLS      output columns per lane in the backward (2, 4)
 //   CSA_BWD_THREADS   backward workgroup size (256, 512, 1024)
 //   CSA_BWD_MAX_WGS   backward grid cap (main workgroups)
 
@@ -76,11 +76,11 @@ int env_int(const char* name, int dflt, const int* allowed, int n_allowed, int l
 const Tuning& tuning() {
   static const Tuning t = [] {
     Tuning d;
-    static const int cols[] = {2, 4, 8};
+    static const int cols[] = {2, 4};
     static const int threads[] = {256, 512, 1024};
-    d.fwd_cols = env_int("CSA_FWD_COLS", d.fwd_cols, cols, 3, 0, 0);
+    d.fwd_cols = env_int("CSA_FWD_COLS", d.fwd_cols, cols, 2, 0, 0);
     d.fwd_max_wgs = env_int("CSA_FWD_MAX_WGS", d.fwd_max_wgs, nullptr, 0, 1, 1 << 20);
-    d.bwd_cols = env_int("CSA_BWD_COLS", d.bwd_cols, cols, 3, 0, 0);
+    d.bwd_cols = env_int("CSA_BWD_COLS", d.bwd_cols, cols, 2, 0, 0);
     d.bwd_threads = env_int("CSA_BWD_THREADS", d.bwd_threads, threads, 3, 0, 0);
     d.bwd_max_wgs = env_int("CSA_BWD_MAX_WGS", d.bwd_max_wgs, nullptr, 0, 1, 1 << 16);
     return d;
@@ -176,7 +176,8 @@ Plan make_plan(const Problem& p) {
   // backward
   {
     const int C = p.head_dim < tu.bwd_cols ? p.head_dim : tu.bwd_cols;
-    const int NT = tu.bwd_threads;
+    // 4 columns per lane need more than 128 VGPRs: at most 512 threads
+    const int NT = (C == 4 && tu.bwd_threads > 512) ? 512 : tu.bwd_threads;
     const int64_t G = p.head_dim / C;
     const int64_t lanes = p.N * G;
     int64_t main = (lanes + NT - 1) / NT;

@@ -215,44 +215,50 @@ __device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t& excl
 }
 
 // Returns true (uniformly across the block) iff cu is a valid pack for
-// (S, T_cap, N).  LDS layout: int64 scratch[NT/64], cu[S+1], off[S+1].
-template <int R, int NT>
+// (S, T_cap, N).  GT = false: the table is built in LDS (layout: int64
+// scratch[NT/64], cu[S+1], off[S+1]) and every later lookup is an LDS read.
+// GT = true: the table was built in the workspace by seg_scan_kernel.  The
+// location is a template parameter so lookups compile to ds_read (LDS) or
+// global_load (workspace), never to flat loads, which would make every
+// lookup wait for all outstanding buffer loads.
+template <int R, int NT, bool GT>
 __device__ bool load_segment_table(const SegParams& sp, int32_t* lds, SegTable& t) {
-  if (sp.global_table) {
+  if constexpr (GT) {
     t.cu = sp.cu;
     t.off = sp.g_off;
     return __builtin_nontemporal_load(sp.g_flag) == 1;
+  } else {
+    const int S = sp.S;
+    int64_t* s_wave = reinterpret_cast<int64_t*>(lds);
+    int32_t* s_cu = lds + 2 * (NT / 64);
+    int32_t* s_off = s_cu + (S + 1);
+    const int tid = threadIdx.x;
+    for (int i = tid; i <= S; i += NT) s_cu[i] = sp.cu[i];
+    __syncthreads();
+    const int per = (S + NT - 1) / NT;
+    const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
+    int64_t local = 0;
+    int bad = 0;
+    for (int s = s0; s < s1; ++s) {
+      const int32_t L = s_cu[s + 1] - s_cu[s];
+      bad |= (L < 0);
+      local += (L > 0) ? (L / R) : 0;
+    }
+    int64_t run;
+    const int64_t total = block_exclusive_scan<NT>(local, run, s_wave);
+    for (int s = s0; s < s1; ++s) {
+      s_off[s] = static_cast<int32_t>(run);
+      const int32_t L = s_cu[s + 1] - s_cu[s];
+      run += (L > 0) ? (L / R) : 0;
+    }
+    if (tid == 0) {
+      s_off[S] = static_cast<int32_t>(total);
+      bad |= (s_cu[0] != 0) | (static_cast<int64_t>(s_cu[S]) > sp.T_cap) | (total != sp.N);
+    }
+    t.cu = s_cu;
+    t.off = s_off;
+    return __syncthreads_or(bad) == 0;
   }
-  const int S = sp.S;
-  int64_t* s_wave = reinterpret_cast<int64_t*>(lds);
-  int32_t* s_cu = lds + 2 * (NT / 64);
-  int32_t* s_off = s_cu + (S + 1);
-  const int tid = threadIdx.x;
-  for (int i = tid; i <= S; i += NT) s_cu[i] = sp.cu[i];
-  __syncthreads();
-  const int per = (S + NT - 1) / NT;
-  const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
-  int64_t local = 0;
-  int bad = 0;
-  for (int s = s0; s < s1; ++s) {
-    const int32_t L = s_cu[s + 1] - s_cu[s];
-    bad |= (L < 0);
-    local += (L > 0) ? (L / R) : 0;
-  }
-  int64_t run;
-  const int64_t total = block_exclusive_scan<NT>(local, run, s_wave);
-  for (int s = s0; s < s1; ++s) {
-    s_off[s] = static_cast<int32_t>(run);
-    const int32_t L = s_cu[s + 1] - s_cu[s];
-    run += (L > 0) ? (L / R) : 0;
-  }
-  if (tid == 0) {
-    s_off[S] = static_cast<int32_t>(total);
-    bad |= (s_cu[0] != 0) | (static_cast<int64_t>(s_cu[S]) > sp.T_cap) | (total != sp.N);
-  }
-  t.cu = s_cu;
-  t.off = s_off;
-  return __syncthreads_or(bad) == 0;
 }
 
 // Largest s in [0, S) with off[s] <= n (requires n < off[S]); skips empty
@@ -267,13 +273,122 @@ __device__ __forceinline__ int find_segment(const int32_t* off, int S, int32_t n
 }
 
 // ---------------------------------------------------------------------------
+// One window's inputs, fetched one window ahead of its use.
+//
+// Every load of a window is issued before any of them is waited on, and the
+// next window's loads are issued before the current window is computed, so
+// each wave keeps two windows of loads in flight.  Loads a window does not
+// need (the previous half of a segment's first block, lanes past the last
+// output row) use an offset at the end of the buffer: the hardware range
+// check returns 0 and touches no memory.
+// ---------------------------------------------------------------------------
+template <int R, int CO, int C, bool BWD>
+struct Window {
+  Pack<C> so[R], vo[R];                    // own rows (second half at coff 2)
+  Pack<C> sp[CO == 2 ? R : 1];             // previous block's rows, first half
+  Pack<C> vp[CO == 2 ? R : 1];
+  Pack<C> gd[BWD ? 1 : 0 + 1];             // dout chunk (backward)
+  uint32_t own;                            // first row of the block
+  uint32_t seg_end;                        // cu[s + 1]
+  bool has_prev;                           // coff 2 and not the segment's first block
+  bool last;                               // the segment's last block
+};
+
+struct WinCtx {
+  const int32_t* cu;
+  const int32_t* off;
+  int S;
+  uint32_t N, W, d, g;
+  uint32_t oob_io, oob_do;                 // past-the-end offsets (masked loads)
+  rsrc_t rkv, rsc, rdo;
+};
+
+template <int R, int CO, int C, bool BWD>
+__device__ __forceinline__ void fetch_window(Window<R, CO, C, BWD>& w, uint32_t n, const WinCtx& x) {
+  const bool valid = n < x.N;
+  uint32_t own = 0, b = 0, nb = 0, end = 0;
+  if (valid) {
+    const int s = find_segment(x.off, x.S, static_cast<int32_t>(n));
+    b = n - x.off[s];
+    nb = x.off[s + 1] - x.off[s];
+    own = x.cu[s] + b * R;
+    end = x.cu[s + 1];
+  }
+  w.own = own;
+  w.seg_end = end;
+  w.has_prev = (CO == 2) && valid && b > 0;
+  w.last = valid && (b + 1 == nb);
+  const uint32_t col_own = (CO - 1) * x.d + x.g * C;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const uint32_t o = valid ? ((own + i) * x.W + col_own) * 2u : x.oob_io;
+    w.so[i] = load_pack<C>(x.rsc, o);
+    w.vo[i] = load_pack<C>(x.rkv, o);
+  }
+  if constexpr (CO == 2) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const uint32_t o = w.has_prev ? ((own - R + i) * x.W + x.g * C) * 2u : x.oob_io;
+      w.sp[i] = load_pack<C>(x.rsc, o);
+      w.vp[i] = load_pack<C>(x.rkv, o);
+    }
+  }
+  if constexpr (BWD) w.gd[0] = load_pack<C>(x.rdo, valid ? (n * x.d + x.g * C) * 2u : x.oob_do);
+}
+
+// Forward of one window: the C output columns packed as bf16.
+template <int R, int CO, int C, bool BWD>
+__device__ __forceinline__ Pack<C> fwd_window(const Window<R, CO, C, BWD>& w, const float (&ape_r)[CO][R][C]) {
+  Pack<C> outp;
+  if (CO == 2 && w.has_prev) {
+    constexpr int K = 2 * R;
+#pragma unroll
+    for (int kp = 0; kp < C / 2; ++kp) {
+      float o2[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int k = 2 * kp + hh;
+        float x[K], v[K], e[K], Rz;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          x[i] = elem<C>(w.sp[i], k) + ape_r[0][i][k];
+          v[i] = elem<C>(w.vp[i], k);
+          x[R + i] = elem<C>(w.so[i], k) + ape_r[CO - 1][i][k];
+          v[R + i] = elem<C>(w.vo[i], k);
+        }
+        o2[hh] = softmax_pool<K>(x, v, e, Rz);
+      }
+      outp.w[kp] = pack_bf16x2(o2[0], o2[1]);
+    }
+  } else {
+#pragma unroll
+    for (int kp = 0; kp < C / 2; ++kp) {
+      float o2[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int k = 2 * kp + hh;
+        float x[R], v[R], e[R], Rz;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          x[i] = elem<C>(w.so[i], k) + ape_r[CO - 1][i][k];
+          v[i] = elem<C>(w.vo[i], k);
+        }
+        o2[hh] = softmax_pool<R>(x, v, e, Rz);
+      }
+      outp.w[kp] = pack_bf16x2(o2[0], o2[1]);
+    }
+  }
+  return outp;
+}
+
+// ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
-template <int R, int CO, int C, int NT>
+template <int R, int CO, int C, int NT, bool GT>
 __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
   extern __shared__ int32_t lds[];
   SegTable tab;
-  if (!load_segment_table<R, NT>(p.seg, lds, tab)) return;
+  if (!load_segment_table<R, NT, GT>(p.seg, lds, tab)) return;
 
   const uint32_t d = p.head_dim, W = CO * d;
   const uint32_t lgG = p.log2_chunks, G = 1u << lgG;
@@ -282,10 +397,21 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
   const uint32_t nstride = (gridDim.x * NT) >> lgG;
   const uint32_t N = static_cast<uint32_t>(p.seg.N);
   uint32_t n = L >> lgG;
-  if (n >= N) return;
+  if (n >= N || nstride == 0) return;
 
-  const rsrc_t rkv = make_rsrc(p.kv, p.io_bytes);
-  const rsrc_t rsc = make_rsrc(p.score, p.io_bytes);
+  WinCtx x;
+  x.cu = tab.cu;
+  x.off = tab.off;
+  x.S = p.seg.S;
+  x.N = N;
+  x.W = W;
+  x.d = d;
+  x.g = g;
+  x.oob_io = p.io_bytes;
+  x.oob_do = 0;
+  x.rkv = make_rsrc(p.kv, p.io_bytes);
+  x.rsc = make_rsrc(p.score, p.io_bytes);
+  x.rdo = x.rkv;
   const rsrc_t rape = make_rsrc(p.ape, R * W * 4u);
   const rsrc_t rout = make_rsrc(p.out, N * d * 2u);
 
@@ -296,64 +422,12 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < R; ++i) load_f32<C>(rape, (i * W + h * d + g * C) * 4u, ape_r[h][i]);
 
-  const uint32_t col_prev = g * C;                   // first half
-  const uint32_t col_own = (CO - 1) * d + g * C;     // second half at coff = 2
+  Window<R, CO, C, false> cur, nxt;
+  fetch_window(cur, n, x);
   for (; n < N; n += nstride) {
-    const int s = find_segment(tab.off, p.seg.S, static_cast<int32_t>(n));
-    const uint32_t b = n - tab.off[s];
-    const uint32_t own = tab.cu[s] + b * R;
-    Pack<C> so[R], vo[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      so[i] = load_pack<C>(rsc, ((own + i) * W + col_own) * 2u);
-      vo[i] = load_pack<C>(rkv, ((own + i) * W + col_own) * 2u);
-    }
-    Pack<C> outp;
-    if (CO == 2 && b > 0) {
-      constexpr int K = CO * R;
-      Pack<C> sp[R], vp[R];
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        sp[i] = load_pack<C>(rsc, ((own - R + i) * W + col_prev) * 2u);
-        vp[i] = load_pack<C>(rkv, ((own - R + i) * W + col_prev) * 2u);
-      }
-#pragma unroll
-      for (int kp = 0; kp < C / 2; ++kp) {
-        float o2[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int k = 2 * kp + hh;
-          float x[K], v[K], e[K], Rz;
-#pragma unroll
-          for (int i = 0; i < R; ++i) {
-            x[i] = elem<C>(sp[i], k) + ape_r[0][i][k];
-            v[i] = elem<C>(vp[i], k);
-            x[R + i] = elem<C>(so[i], k) + ape_r[CO - 1][i][k];
-            v[R + i] = elem<C>(vo[i], k);
-          }
-          o2[hh] = softmax_pool<K>(x, v, e, Rz);
-        }
-        outp.w[kp] = pack_bf16x2(o2[0], o2[1]);
-      }
-    } else {
-#pragma unroll
-      for (int kp = 0; kp < C / 2; ++kp) {
-        float o2[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int k = 2 * kp + hh;
-          float x[R], v[R], e[R], Rz;
-#pragma unroll
-          for (int i = 0; i < R; ++i) {
-            x[i] = elem<C>(so[i], k) + ape_r[CO - 1][i][k];
-            v[i] = elem<C>(vo[i], k);
-          }
-          o2[hh] = softmax_pool<R>(x, v, e, Rz);
-        }
-        outp.w[kp] = pack_bf16x2(o2[0], o2[1]);
-      }
-    }
-    store_pack<C>(rout, (n * d + g * C) * 2u, outp);
+    fetch_window(nxt, n + nstride, x);
+    store_pack<C>(rout, (n * d + g * C) * 2u, fwd_window(cur, ape_r));
+    cur = nxt;
   }
 }
 
@@ -397,12 +471,12 @@ __device__ void zero_sweep(const BwdParams& p, const SegTable& tab) {
   zero_range(rdsc, b0, b1, zid * NT + threadIdx.x, nz * NT);
 }
 
-template <int R, int CO, int C, int NT>
+template <int R, int CO, int C, int NT, bool GT>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   extern __shared__ int32_t lds[];
   SegTable tab;
-  const bool valid = load_segment_table<R, NT>(p.seg, lds, tab);
-  if (blockIdx.x == 0 && threadIdx.x == 0 && !p.seg.global_table)
+  const bool valid = load_segment_table<R, NT, GT>(p.seg, lds, tab);
+  if (!GT && blockIdx.x == 0 && threadIdx.x == 0)
     __builtin_nontemporal_store(valid ? 1 : 0, p.ws_flag);
   if (!valid) return;
   if (blockIdx.x >= p.main_wgs) {
@@ -435,28 +509,31 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       for (int k = 0; k < C; ++k) acc_r[h][i][k] = 0.0f;
     }
 
+  WinCtx x;
+  x.cu = tab.cu;
+  x.off = tab.off;
+  x.S = p.seg.S;
+  x.N = N;
+  x.W = W;
+  x.d = d;
+  x.g = g;
+  x.oob_io = p.io_bytes;
+  x.oob_do = N * d * 2u;
+  x.rkv = rkv;
+  x.rsc = rsc;
+  x.rdo = rdo;
+
   const uint32_t col_prev = g * C;
   const uint32_t col_own = (CO - 1) * d + g * C;
-  for (uint32_t n = L >> lgG; n < N; n += nstride) {
-    const int s = find_segment(tab.off, p.seg.S, static_cast<int32_t>(n));
-    const uint32_t b = n - tab.off[s];
-    const uint32_t nb = tab.off[s + 1] - tab.off[s];
-    const uint32_t own = tab.cu[s] + b * R;
-    const Pack<C> gp = load_pack<C>(rdo, (n * d + g * C) * 2u);
-    Pack<C> so[R], vo[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      so[i] = load_pack<C>(rsc, ((own + i) * W + col_own) * 2u);
-      vo[i] = load_pack<C>(rkv, ((own + i) * W + col_own) * 2u);
-    }
-    if (CO == 2 && b > 0) {
-      constexpr int K = CO * R;
-      Pack<C> sp[R], vp[R];
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        sp[i] = load_pack<C>(rsc, ((own - R + i) * W + col_prev) * 2u);
-        vp[i] = load_pack<C>(rkv, ((own - R + i) * W + col_prev) * 2u);
-      }
+  uint32_t n = L >> lgG;
+  Window<R, CO, C, true> cur, nxt;
+  fetch_window(cur, n, x);
+  for (; n < N && nstride != 0; n += nstride) {
+    fetch_window(nxt, n + nstride, x);
+    const uint32_t own = cur.own;
+    const Pack<C>& gp = cur.gd[0];
+    if (CO == 2 && cur.has_prev) {
+      constexpr int K = 2 * R;
       Pack<C> gkv[K], gsc[K];
 #pragma unroll
       for (int kp = 0; kp < C / 2; ++kp) {
@@ -464,15 +541,15 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int k = 2 * kp + hh;
-          float x[K], v[K], e[K], Rz;
+          float xs[K], v[K], e[K], Rz;
 #pragma unroll
           for (int i = 0; i < R; ++i) {
-            x[i] = elem<C>(sp[i], k) + ape_r[0][i][k];
-            v[i] = elem<C>(vp[i], k);
-            x[R + i] = elem<C>(so[i], k) + ape_r[CO - 1][i][k];
-            v[R + i] = elem<C>(vo[i], k);
+            xs[i] = elem<C>(cur.sp[i], k) + ape_r[0][i][k];
+            v[i] = elem<C>(cur.vp[i], k);
+            xs[R + i] = elem<C>(cur.so[i], k) + ape_r[CO - 1][i][k];
+            v[R + i] = elem<C>(cur.vo[i], k);
           }
-          const float o = softmax_pool<K>(x, v, e, Rz);
+          const float o = softmax_pool<K>(xs, v, e, Rz);
           const float Gk = Rz * elem<C>(gp, k);
 #pragma unroll
           for (int i = 0; i < K; ++i) {
@@ -508,13 +585,13 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int k = 2 * kp + hh;
-          float x[R], v[R], e[R], Rz;
+          float xs[R], v[R], e[R], Rz;
 #pragma unroll
           for (int i = 0; i < R; ++i) {
-            x[i] = elem<C>(so[i], k) + ape_r[CO - 1][i][k];
-            v[i] = elem<C>(vo[i], k);
+            xs[i] = elem<C>(cur.so[i], k) + ape_r[CO - 1][i][k];
+            v[i] = elem<C>(cur.vo[i], k);
           }
-          const float o = softmax_pool<R>(x, v, e, Rz);
+          const float o = softmax_pool<R>(xs, v, e, Rz);
           const float Gk = Rz * elem<C>(gp, k);
 #pragma unroll
           for (int i = 0; i < R; ++i) {
@@ -537,7 +614,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         store_pack<C>(rdsc, ((own + i) * W + col_own) * 2u, gsc[i]);
       }
     }
-    if (b + 1 == nb) {
+    if (cur.last) {
       // The segment's last block owns the never-read slots next to it.
       Pack<C> z;
 #pragma unroll
@@ -549,7 +626,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
           store_pack<C>(rdsc, ((own + i) * W + col_prev) * 2u, z);
         }
       }
-      for (uint32_t t = own + R; t < static_cast<uint32_t>(tab.cu[s + 1]); ++t) {
+      for (uint32_t t = own + R; t < cur.seg_end; ++t) {
 #pragma unroll
         for (int h = 0; h < CO; ++h) {
           store_pack<C>(rdkv, (t * W + h * d + g * C) * 2u, z);
@@ -557,6 +634,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         }
       }
     }
+    cur = nxt;
   }
 
   // ---- dAPE: fixed-order reduction inside the workgroup ----
@@ -686,18 +764,25 @@ __global__ __launch_bounds__(kScanNT) void seg_scan_kernel(SegParams sp, int32_t
 // ---------------------------------------------------------------------------
 template <int R, int CO, int C>
 static void launch_fwd_rcc(const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads>), dim3(sh.grid), dim3(kFwdThreads), sh.lds_bytes, st, p);
+  if (p.seg.global_table)
+    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, true>), dim3(sh.grid), dim3(kFwdThreads), sh.lds_bytes,
+                       st, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, false>), dim3(sh.grid), dim3(kFwdThreads), sh.lds_bytes,
+                       st, p);
 }
 
 template <int R, int CO, int C, int NT>
 static void launch_bwd_rccn(const BwdParams& p, const LaunchShape& sh, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT>), dim3(sh.grid), dim3(NT), sh.lds_bytes, st, p);
+  if (p.seg.global_table)
+    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, true>), dim3(sh.grid), dim3(NT), sh.lds_bytes, st, p);
+  else
+    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, false>), dim3(sh.grid), dim3(NT), sh.lds_bytes, st, p);
 }
 
 template <int R, int CO>
 static bool launch_fwd_rc(const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
   switch (sh.cols) {
-    case 8: launch_fwd_rcc<R, CO, 8>(p, sh, st); return true;
     case 4: launch_fwd_rcc<R, CO, 4>(p, sh, st); return true;
     case 2: launch_fwd_rcc<R, CO, 2>(p, sh, st); return true;
   }
@@ -717,7 +802,6 @@ static bool launch_bwd_rcc(const BwdParams& p, const LaunchShape& sh, hipStream_
 template <int R, int CO>
 static bool launch_bwd_rc(const BwdParams& p, const LaunchShape& sh, hipStream_t st) {
   switch (sh.cols) {
-    case 8: return launch_bwd_rcc<R, CO, 8>(p, sh, st);
     case 4: return launch_bwd_rcc<R, CO, 4>(p, sh, st);
     case 2: return launch_bwd_rcc<R, CO, 2>(p, sh, st);
   }
