@@ -21,6 +21,8 @@
 //   CSA_BWD_COLS      output columns per lane in the backward (2, 4)
 //   CSA_BWD_THREADS   backward workgroup size (256, 512, 1024)
 //   CSA_BWD_MAX_WGS   backward grid cap (main workgroups)
+//   CSA_BWD_SLICE_BYTES  bytes of a half-row one backward workgroup covers
+//                     (>= 128; smaller slices shrink the dAPE partials)
 
 #include <stdarg.h>
 #include <stdio.h>
@@ -57,6 +59,7 @@ struct Tuning {
   int bwd_cols = 2;
   int bwd_threads = 1024;
   int bwd_max_wgs = 256;
+  int bwd_slice_bytes = 128;
 };
 
 int env_int(const char* name, int dflt, const int* allowed, int n_allowed, int lo, int hi) {
@@ -83,6 +86,7 @@ const Tuning& tuning() {
     d.bwd_cols = env_int("CSA_BWD_COLS", d.bwd_cols, cols, 2, 0, 0);
     d.bwd_threads = env_int("CSA_BWD_THREADS", d.bwd_threads, threads, 3, 0, 0);
     d.bwd_max_wgs = env_int("CSA_BWD_MAX_WGS", d.bwd_max_wgs, nullptr, 0, 1, 1 << 16);
+    d.bwd_slice_bytes = env_int("CSA_BWD_SLICE_BYTES", d.bwd_slice_bytes, nullptr, 0, 16, 1 << 16);
     return d;
   }();
   return t;
@@ -141,6 +145,7 @@ struct Plan {
   // backward
   csa::LaunchShape bwd;
   int bwd_log2_chunks;
+  int bwd_log2_slice;
   uint32_t bwd_main_wgs;
   uint32_t partial_rows;
   uint32_t lds_table_words;
@@ -179,11 +184,17 @@ Plan make_plan(const Problem& p) {
     // 4 columns per lane need more than 128 VGPRs: at most 512 threads
     const int NT = (C == 4 && tu.bwd_threads > 512) ? 512 : tu.bwd_threads;
     const int64_t G = p.head_dim / C;
+    // column slice per workgroup: at least 128 bytes of a half-row per wave
+    // row (whole cache lines), at most the whole row and the workgroup
+    int64_t CS = tu.bwd_slice_bytes / (2 * C);
+    if (CS < 64 / C) CS = 64 / C;
+    if (CS > G) CS = G;
+    if (CS > NT) CS = NT;
+    const int64_t slices = G / CS;
     const int64_t lanes = p.N * G;
     int64_t main = (lanes + NT - 1) / NT;
     if (main > tu.bwd_max_wgs) main = tu.bwd_max_wgs;
-    const int64_t slices = G > NT ? G / NT : 1;
-    main = align_up(main, slices);  // lanes % G == 0 and whole partial rows
+    main = align_up(main, slices);  // whole slices
     // zero-fill workgroups for rows of segments shorter than ratio and rows
     // past cu[S]: at most total_tokens - total_comp*ratio rows qualify
     const int64_t spare_rows = p.T - p.N * p.ratio;
@@ -199,11 +210,11 @@ Plan make_plan(const Problem& p) {
     pl.bwd.threads = NT;
     pl.bwd.cols = C;
     pl.bwd_log2_chunks = log2i(G);
+    pl.bwd_log2_slice = log2i(CS);
     pl.bwd_main_wgs = static_cast<uint32_t>(main);
     pl.partial_rows = static_cast<uint32_t>(main / slices);
     pl.lds_table_words = pl.global_table ? 0 : static_cast<uint32_t>(2 * (NT / 64) + 2 * (p.S + 1));
-    const int64_t wg_chunks = G < NT ? G : NT;
-    const uint64_t red_floats = uint64_t(p.coff) * p.ratio * wg_chunks * C;
+    const uint64_t red_floats = uint64_t(p.coff) * p.ratio * CS * C;
     pl.bwd.lds_bytes = (uint64_t(pl.lds_table_words) + red_floats) * 4;
     pl.partial_offset = kHeaderBytes + pl.off_bytes;
     pl.ws_bwd = pl.partial_offset + align_up(uint64_t(pl.partial_rows) * p.ratio * W * 4, 256);
@@ -291,6 +302,7 @@ csa_status_t launch_bwd_grads(const Problem& pr, const Plan& pl, const void* kv,
   bp.io_bytes = static_cast<uint32_t>(pr.T * pr.coff * pr.head_dim * 2);
   bp.head_dim = pr.head_dim;
   bp.log2_chunks = pl.bwd_log2_chunks;
+  bp.log2_slice = pl.bwd_log2_slice;
   bp.main_wgs = pl.bwd_main_wgs;
   bp.partial_rows = pl.partial_rows;
   bp.lds_table_words = pl.lds_table_words;

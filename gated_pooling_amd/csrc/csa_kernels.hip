@@ -484,11 +484,21 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     return;
   }
 
+  // Lane mapping: the G chunks of a row are split into slices of CS chunks
+  // (CS * C * 2 >= 128 bytes, so a wave still reads whole cache lines).  A
+  // workgroup owns one slice and NT / CS window rows at a time, so its dAPE
+  // partial covers only its slice's columns: the partial buffer is
+  // (workgroups per slice) x ratio x W floats instead of workgroups x ratio x W.
   const uint32_t d = p.head_dim, W = CO * d;
-  const uint32_t lgG = p.log2_chunks, G = 1u << lgG;
-  const uint32_t L = blockIdx.x * NT + threadIdx.x;
-  const uint32_t g = L & (G - 1);
-  const uint32_t nstride = (p.main_wgs * NT) >> lgG;
+  const uint32_t lgG = p.log2_chunks;
+  const uint32_t lgCS = p.log2_slice, CS = 1u << lgCS;
+  const uint32_t lgSl = lgG - lgCS;                        // log2(slices)
+  const uint32_t slice = blockIdx.x & ((1u << lgSl) - 1);
+  const uint32_t wg_in_slice = blockIdx.x >> lgSl;
+  const uint32_t wgs_per_slice = p.main_wgs >> lgSl;
+  const uint32_t g = (slice << lgCS) + (threadIdx.x & (CS - 1));
+  const uint32_t rows_per_wg = NT >> lgCS;
+  const uint32_t nstride = wgs_per_slice * rows_per_wg;
   const uint32_t N = static_cast<uint32_t>(p.seg.N);
 
   const rsrc_t rkv = make_rsrc(p.kv, p.io_bytes);
@@ -525,7 +535,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 
   const uint32_t col_prev = g * C;
   const uint32_t col_own = (CO - 1) * d + g * C;
-  uint32_t n = L >> lgG;
+  uint32_t n = wg_in_slice * rows_per_wg + (threadIdx.x >> lgCS);
   Window<R, CO, C, true> cur, nxt;
   fetch_window(cur, n, x);
   for (; n < N && nstride != 0; n += nstride) {
@@ -638,9 +648,9 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   }
 
   // ---- dAPE: fixed-order reduction inside the workgroup ----
-  // 1) lanes of a wave that share a chunk (chunks < 64): xor butterfly.
-  if (G < 64) {
-    for (uint32_t o = G; o < 64; o <<= 1) {
+  // 1) lanes of a wave that share a chunk (CS < 64): xor butterfly.
+  if (CS < 64) {
+    for (uint32_t o = CS; o < 64; o <<= 1) {
 #pragma unroll
       for (int h = 0; h < CO; ++h)
 #pragma unroll
@@ -649,17 +659,16 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
           for (int k = 0; k < C; ++k) acc_r[h][i][k] += __shfl_xor(acc_r[h][i][k], o, 64);
     }
   }
-  // 2) waves in index order into LDS red[h][i][c], c over the chunks this
-  //    workgroup covers (all G chunks when G <= NT, else a slice of NT).
-  const uint32_t wg_chunks = G < NT ? G : NT;
-  const uint32_t CW = wg_chunks * C;
+  // 2) waves in index order into LDS red[h][i][c], c over the slice's CS*C
+  //    columns (per half).
+  const uint32_t CW = CS * C;
   float* red = reinterpret_cast<float*>(lds + p.lds_table_words);
   for (uint32_t idx = threadIdx.x; idx < CO * R * CW; idx += NT) red[idx] = 0.0f;
   __syncthreads();
   const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t gl = g & (wg_chunks - 1);
+  const uint32_t gl = threadIdx.x & (CS - 1);
   for (uint32_t w = 0; w < NT / 64; ++w) {
-    if (wave == w && (G >= 64 || lane < G)) {
+    if (wave == w && (CS >= 64 || lane < CS)) {
 #pragma unroll
       for (int h = 0; h < CO; ++h)
 #pragma unroll
@@ -669,16 +678,14 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     }
     __syncthreads();
   }
-  // 3) one partial row per (workgroup / slice): partial[row][i][h*d + col]
-  const uint32_t slices = G / wg_chunks;
-  const uint32_t prow = blockIdx.x / slices;
-  const uint32_t cbase = (blockIdx.x % slices) * CW;
+  // 3) one partial row per workgroup of a slice: partial[row][i][h*d + col]
+  const uint32_t cbase = slice * CW;
   const rsrc_t rpart = make_rsrc(p.partials, p.partial_rows * R * W * 4u);
   for (uint32_t idx = threadIdx.x; idx < CO * R * CW; idx += NT) {
     const uint32_t hi = idx / CW, c = idx - hi * CW;
     const uint32_t h = hi / R, i = hi - h * R;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(red[idx]), rpart,
-                                          ((prow * R + i) * W + h * d + cbase + c) * 4u, 0, 0);
+                                          ((wg_in_slice * R + i) * W + h * d + cbase + c) * 4u, 0, 0);
   }
 }
 

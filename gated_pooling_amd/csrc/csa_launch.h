@@ -47,8 +47,9 @@ struct BwdParams {
   uint32_t io_bytes;
   uint32_t head_dim;
   uint32_t log2_chunks;
+  uint32_t log2_slice;    // log2(chunks per workgroup column slice)
   uint32_t main_wgs;      // workgroups [0, main_wgs) compute windows, the rest zero-fill
-  uint32_t partial_rows;
+  uint32_t partial_rows;  // main_wgs / slices
   uint32_t lds_table_words;
 };
 
