@@ -180,6 +180,87 @@ __device__ __forceinline__ float softmax_pool(const float (&x)[K], const float (
   return acc * R;
 }
 
+// NC columns of one window at once, same arithmetic as softmax_pool per
+// column.  Written stage by stage across all NC*K entries (each Horner step
+// for every entry before the next step) so a wave has NC*K independent
+// chains to issue instead of one long dependent chain per entry.
+template <int NC, int K>
+__device__ __forceinline__ void softmax_pool_cols(const float (&x)[NC][K], const float (&v)[NC][K],
+                                                  float (&e)[NC][K], float (&R)[NC], float (&o)[NC]) {
+  constexpr float kLog2e = 1.44269504088896340736f;
+  constexpr float kLn2Hi = 0.693147180559945309417f;
+  constexpr float kLn2Lo = -1.904654299957768e-09f;  // ln 2 - fp32(ln 2)
+  float m[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) m[c] = x[c][0];
+#pragma unroll
+  for (int k = 1; k < K; ++k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) m[c] = fmaxf(m[c], x[c][k]);
+  float y[NC][K], kf[NC][K], q[NC][K];
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) y[c][k] = fmaxf(x[c][k] - m[c], -104.0f);
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kf[c][k] = __builtin_rintf(y[c][k] * kLog2e);
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) y[c][k] = __builtin_fmaf(-kf[c][k], kLn2Hi, y[c][k]);
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) y[c][k] = __builtin_fmaf(-kf[c][k], kLn2Lo, y[c][k]);  // y now holds r
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) q[c][k] = __builtin_fmaf(1.0f / 720.0f, y[c][k], 1.0f / 120.0f);
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) q[c][k] = __builtin_fmaf(q[c][k], y[c][k], 1.0f / 24.0f);
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) q[c][k] = __builtin_fmaf(q[c][k], y[c][k], 1.0f / 6.0f);
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) q[c][k] = __builtin_fmaf(q[c][k], y[c][k], 0.5f);
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) q[c][k] = __builtin_fmaf(q[c][k], y[c][k], 1.0f);
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) q[c][k] = __builtin_fmaf(q[c][k], y[c][k], 1.0f);
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) e[c][k] = __builtin_ldexpf(q[c][k], static_cast<int>(kf[c][k]));
+  float Z[NC], acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    Z[c] = e[c][0];
+    acc[c] = __builtin_fmaf(e[c][0], v[c][0], 0.0f);
+  }
+#pragma unroll
+  for (int k = 1; k < K; ++k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      Z[c] = Z[c] + e[c][k];
+      acc[c] = __builtin_fmaf(e[c][k], v[c][k], acc[c]);
+    }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) R[c] = 1.0f / Z[c];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) o[c] = acc[c] * R[c];
+}
+
 // ---------------------------------------------------------------------------
 // Segment table: cu_seqlens and the exclusive scan of floor(L_s / ratio)
 // (output-block offsets), validated.  Small packs: built per workgroup in
@@ -344,37 +425,35 @@ __device__ __forceinline__ Pack<C> fwd_window(const Window<R, CO, C, BWD>& w, co
     constexpr int K = 2 * R;
 #pragma unroll
     for (int kp = 0; kp < C / 2; ++kp) {
-      float o2[2];
+      float x[2][K], v[2][K], e[2][K], Rz[2], o2[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int k = 2 * kp + hh;
-        float x[K], v[K], e[K], Rz;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-          x[i] = elem<C>(w.sp[i], k) + ape_r[0][i][k];
-          v[i] = elem<C>(w.vp[i], k);
-          x[R + i] = elem<C>(w.so[i], k) + ape_r[CO - 1][i][k];
-          v[R + i] = elem<C>(w.vo[i], k);
+          x[hh][i] = elem<C>(w.sp[i], k) + ape_r[0][i][k];
+          v[hh][i] = elem<C>(w.vp[i], k);
+          x[hh][R + i] = elem<C>(w.so[i], k) + ape_r[CO - 1][i][k];
+          v[hh][R + i] = elem<C>(w.vo[i], k);
         }
-        o2[hh] = softmax_pool<K>(x, v, e, Rz);
       }
+      softmax_pool_cols<2, K>(x, v, e, Rz, o2);
       outp.w[kp] = pack_bf16x2(o2[0], o2[1]);
     }
   } else {
 #pragma unroll
     for (int kp = 0; kp < C / 2; ++kp) {
-      float o2[2];
+      float x[2][R], v[2][R], e[2][R], Rz[2], o2[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int k = 2 * kp + hh;
-        float x[R], v[R], e[R], Rz;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-          x[i] = elem<C>(w.so[i], k) + ape_r[CO - 1][i][k];
-          v[i] = elem<C>(w.vo[i], k);
+          x[hh][i] = elem<C>(w.so[i], k) + ape_r[CO - 1][i][k];
+          v[hh][i] = elem<C>(w.vo[i], k);
         }
-        o2[hh] = softmax_pool<R>(x, v, e, Rz);
       }
+      softmax_pool_cols<2, R>(x, v, e, Rz, o2);
       outp.w[kp] = pack_bf16x2(o2[0], o2[1]);
     }
   }
@@ -548,23 +627,27 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 #pragma unroll
       for (int kp = 0; kp < C / 2; ++kp) {
         float a2[2][K], ds2[2][K];
+        float xs[2][K], v[2][K], e[2][K], Rz[2], o2[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int k = 2 * kp + hh;
-          float xs[K], v[K], e[K], Rz;
 #pragma unroll
           for (int i = 0; i < R; ++i) {
-            xs[i] = elem<C>(cur.sp[i], k) + ape_r[0][i][k];
-            v[i] = elem<C>(cur.vp[i], k);
-            xs[R + i] = elem<C>(cur.so[i], k) + ape_r[CO - 1][i][k];
-            v[R + i] = elem<C>(cur.vo[i], k);
+            xs[hh][i] = elem<C>(cur.sp[i], k) + ape_r[0][i][k];
+            v[hh][i] = elem<C>(cur.vp[i], k);
+            xs[hh][R + i] = elem<C>(cur.so[i], k) + ape_r[CO - 1][i][k];
+            v[hh][R + i] = elem<C>(cur.vo[i], k);
           }
-          const float o = softmax_pool<K>(xs, v, e, Rz);
-          const float Gk = Rz * elem<C>(gp, k);
+        }
+        softmax_pool_cols<2, K>(xs, v, e, Rz, o2);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int k = 2 * kp + hh;
+          const float Gk = Rz[hh] * elem<C>(gp, k);
 #pragma unroll
           for (int i = 0; i < K; ++i) {
-            const float a = e[i] * Gk;
-            const float ds = a * (v[i] - o);
+            const float a = e[hh][i] * Gk;
+            const float ds = a * (v[hh][i] - o2[hh]);
             a2[hh][i] = a;
             ds2[hh][i] = ds;
           }
@@ -592,21 +675,25 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 #pragma unroll
       for (int kp = 0; kp < C / 2; ++kp) {
         float a2[2][R], ds2[2][R];
+        float xs[2][R], v[2][R], e[2][R], Rz[2], o2[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int k = 2 * kp + hh;
-          float xs[R], v[R], e[R], Rz;
 #pragma unroll
           for (int i = 0; i < R; ++i) {
-            xs[i] = elem<C>(cur.so[i], k) + ape_r[CO - 1][i][k];
-            v[i] = elem<C>(cur.vo[i], k);
+            xs[hh][i] = elem<C>(cur.so[i], k) + ape_r[CO - 1][i][k];
+            v[hh][i] = elem<C>(cur.vo[i], k);
           }
-          const float o = softmax_pool<R>(xs, v, e, Rz);
-          const float Gk = Rz * elem<C>(gp, k);
+        }
+        softmax_pool_cols<2, R>(xs, v, e, Rz, o2);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int k = 2 * kp + hh;
+          const float Gk = Rz[hh] * elem<C>(gp, k);
 #pragma unroll
           for (int i = 0; i < R; ++i) {
-            const float a = e[i] * Gk;
-            const float ds = a * (v[i] - o);
+            const float a = e[hh][i] * Gk;
+            const float ds = a * (v[hh][i] - o2[hh]);
             a2[hh][i] = a;
             ds2[hh][i] = ds;
             acc_r[CO - 1][i][k] += ds;
