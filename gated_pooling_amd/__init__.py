@@ -76,11 +76,11 @@ def lib():
             f.restype = st
             f.argtypes = [i32, i32, i32, i32, i64, i64, P]
         L.csa_compressor_fwd.restype = st
-        L.csa_compressor_fwd.argtypes = [P, P, P, P, i32, i64, i64, i32, i32, i32, P, P, sz, P]
+        L.csa_compressor_fwd.argtypes = [P, P, P, P, P, i32, i64, i64, i32, i32, i32, P, P, sz, P]
         L.csa_compressor_bwd.restype = st
-        L.csa_compressor_bwd.argtypes = [P, P, P, P, i32, i64, i64, i32, i32, i32, P, P, P, P, i32, P, sz, P]
+        L.csa_compressor_bwd.argtypes = [P, P, P, P, P, i32, i64, i64, i32, i32, i32, P, P, P, P, i32, P, sz, P]
         L.csa_compressor_bwd_grads.restype = st
-        L.csa_compressor_bwd_grads.argtypes = [P, P, P, P, i32, i64, i64, i32, i32, i32, P, P, P, P, sz, P]
+        L.csa_compressor_bwd_grads.argtypes = [P, P, P, P, P, i32, i64, i64, i32, i32, i32, P, P, P, P, sz, P]
         L.csa_compressor_bwd_dape_reduce.restype = st
         L.csa_compressor_bwd_dape_reduce.argtypes = [i32, i32, i32, i32, i64, i64, P, P, sz, P]
         _lib = L
@@ -146,24 +146,26 @@ def csa_compressor_bwd_workspace_size(ratio, coff, head_dim, num_segments, total
     return int(out.value)
 
 
-def csa_compressor_fwd(kv, score, ape, cu_seqlens, num_segments, total_tokens, total_comp, ratio, coff,
-                       head_dim, out, workspace, workspace_bytes, stream) -> None:
-    _check(lib().csa_compressor_fwd(kv, score, ape, cu_seqlens, num_segments, total_tokens, total_comp, ratio, coff,
-                                    head_dim, out, workspace, workspace_bytes, stream), "csa_compressor_fwd")
+def csa_compressor_fwd(kv, score, ape, cu_seqlens, cu_seqlens_host, num_segments, total_tokens, total_comp, ratio,
+                       coff, head_dim, out, workspace, workspace_bytes, stream) -> None:
+    _check(lib().csa_compressor_fwd(kv, score, ape, cu_seqlens, cu_seqlens_host, num_segments, total_tokens,
+                                    total_comp, ratio, coff, head_dim, out, workspace, workspace_bytes, stream),
+           "csa_compressor_fwd")
 
 
-def csa_compressor_bwd(kv, score, ape, cu_seqlens, num_segments, total_tokens, total_comp, ratio, coff, head_dim,
-                       dout, dkv, dscore, dape, deterministic, workspace, workspace_bytes, stream) -> None:
-    _check(lib().csa_compressor_bwd(kv, score, ape, cu_seqlens, num_segments, total_tokens, total_comp, ratio, coff,
-                                    head_dim, dout, dkv, dscore, dape, deterministic, workspace, workspace_bytes,
-                                    stream), "csa_compressor_bwd")
+def csa_compressor_bwd(kv, score, ape, cu_seqlens, cu_seqlens_host, num_segments, total_tokens, total_comp, ratio,
+                       coff, head_dim, dout, dkv, dscore, dape, deterministic, workspace, workspace_bytes,
+                       stream) -> None:
+    _check(lib().csa_compressor_bwd(kv, score, ape, cu_seqlens, cu_seqlens_host, num_segments, total_tokens,
+                                    total_comp, ratio, coff, head_dim, dout, dkv, dscore, dape, deterministic,
+                                    workspace, workspace_bytes, stream), "csa_compressor_bwd")
 
 
-def csa_compressor_bwd_grads(kv, score, ape, cu_seqlens, num_segments, total_tokens, total_comp, ratio, coff,
-                             head_dim, dout, dkv, dscore, workspace, workspace_bytes, stream) -> None:
-    _check(lib().csa_compressor_bwd_grads(kv, score, ape, cu_seqlens, num_segments, total_tokens, total_comp, ratio,
-                                          coff, head_dim, dout, dkv, dscore, workspace, workspace_bytes, stream),
-           "csa_compressor_bwd_grads")
+def csa_compressor_bwd_grads(kv, score, ape, cu_seqlens, cu_seqlens_host, num_segments, total_tokens, total_comp,
+                             ratio, coff, head_dim, dout, dkv, dscore, workspace, workspace_bytes, stream) -> None:
+    _check(lib().csa_compressor_bwd_grads(kv, score, ape, cu_seqlens, cu_seqlens_host, num_segments, total_tokens,
+                                          total_comp, ratio, coff, head_dim, dout, dkv, dscore, workspace,
+                                          workspace_bytes, stream), "csa_compressor_bwd_grads")
 
 
 def csa_compressor_bwd_dape_reduce(ratio, coff, head_dim, num_segments, total_tokens, total_comp, dape, workspace,
@@ -214,9 +216,18 @@ def workspace(nbytes: int, device):
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
+def host_cu(cu_seqlens_host):
+    """A ctypes int32 array holding a host copy of cu_seqlens (or NULL)."""
+    if cu_seqlens_host is None:
+        return ctypes.c_void_p(0)
+    vals = [int(x) for x in cu_seqlens_host]
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
 def compressor_fwd(kv, score, ape, cu_seqlens, ratio: int, coff: int, total_comp: int, out=None, ws=None,
-                   stream=None):
-    """out[total_comp, head_dim] (bf16).  cu_seqlens: int32 GPU tensor."""
+                   stream=None, cu_seqlens_host=None):
+    """out[total_comp, head_dim] (bf16).  cu_seqlens: int32 GPU tensor;
+    cu_seqlens_host: optional host copy (list or CPU tensor) of the same."""
     torch = _torch()
     T, d, S = _problem(kv, ape, cu_seqlens, ratio, coff)
     W = coff * d
@@ -227,14 +238,14 @@ def compressor_fwd(kv, score, ape, cu_seqlens, ratio: int, coff: int, total_comp
         ws = workspace(nbytes, kv.device)
     csa_compressor_fwd(_dev(kv, torch.bfloat16, "kv", (T, W)), _dev(score, torch.bfloat16, "score", (T, W)),
                        _dev(ape, torch.float32, "ape", (ratio, W)), _dev(cu_seqlens, torch.int32, "cu_seqlens"),
-                       S, T, total_comp, ratio, coff, d, _dev(out, torch.bfloat16, "out", (total_comp, d)),
+                       host_cu(cu_seqlens_host), S, T, total_comp, ratio, coff, d, _dev(out, torch.bfloat16, "out", (total_comp, d)),
                        ctypes.c_void_p(ws.data_ptr() if ws is not None else 0),
                        ws.numel() if ws is not None else 0, _stream_ptr(stream))
     return out
 
 
 def compressor_bwd(kv, score, ape, cu_seqlens, ratio: int, coff: int, total_comp: int, dout, dkv=None,
-                   dscore=None, dape=None, ws=None, stream=None, deterministic: int = 1):
+                   dscore=None, dape=None, ws=None, stream=None, deterministic: int = 1, cu_seqlens_host=None):
     """(dkv, dscore, dape): bf16 [T, coff*d] x2 (fully written), fp32 [ratio, coff*d]."""
     torch = _torch()
     T, d, S = _problem(kv, ape, cu_seqlens, ratio, coff)
@@ -250,7 +261,7 @@ def compressor_bwd(kv, score, ape, cu_seqlens, ratio: int, coff: int, total_comp
         ws = workspace(nbytes, kv.device)
     csa_compressor_bwd(_dev(kv, torch.bfloat16, "kv", (T, W)), _dev(score, torch.bfloat16, "score", (T, W)),
                        _dev(ape, torch.float32, "ape", (ratio, W)), _dev(cu_seqlens, torch.int32, "cu_seqlens"),
-                       S, T, total_comp, ratio, coff, d, _dev(dout, torch.bfloat16, "dout", (total_comp, d)),
+                       host_cu(cu_seqlens_host), S, T, total_comp, ratio, coff, d, _dev(dout, torch.bfloat16, "dout", (total_comp, d)),
                        _dev(dkv, torch.bfloat16, "dkv", (T, W)), _dev(dscore, torch.bfloat16, "dscore", (T, W)),
                        _dev(dape, torch.float32, "dape", (ratio, W)), deterministic,
                        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_ptr(stream))

@@ -230,16 +230,43 @@ csa_status_t check_ptr(const void* p, const char* name) {
   return CSA_STATUS_SUCCESS;
 }
 
-csa::SegParams seg_params(const Problem& p, const Plan& pl, const int32_t* cu, void* ws) {
+// Host copy of cu_seqlens (optional): must describe the same pack as the
+// problem; checked here so the kernels can trust it.
+csa_status_t check_host_cu(const Problem& p, const int32_t* cu_host) {
+  if (!cu_host) return CSA_STATUS_SUCCESS;
+  if (cu_host[0] != 0) return fail(CSA_STATUS_INVALID_VALUE, "cu_seqlens_host[0] must be 0");
+  int64_t n = 0;
+  for (int32_t s = 0; s < p.S; ++s) {
+    const int64_t L = int64_t{cu_host[s + 1]} - cu_host[s];
+    if (L < 0) return fail(CSA_STATUS_INVALID_VALUE, "cu_seqlens_host decreases at %d", s);
+    n += L / p.ratio;
+  }
+  if (cu_host[p.S] > p.T) return fail(CSA_STATUS_INVALID_VALUE, "cu_seqlens_host[S] exceeds total_tokens");
+  if (n != p.N)
+    return fail(CSA_STATUS_INVALID_VALUE, "cu_seqlens_host gives %lld output rows, total_comp is %lld", (long long)n,
+                (long long)p.N);
+  return CSA_STATUS_SUCCESS;
+}
+
+csa::SegParams seg_params(const Problem& p, const Plan& pl, const int32_t* cu, const int32_t* cu_host, void* ws) {
   csa::SegParams sp{};
   sp.cu = cu;
   sp.T_cap = p.T;
   sp.N = p.N;
   sp.S = p.S;
-  sp.global_table = pl.global_table ? 1 : 0;
+  sp.table = csa::kTableLds;
   if (pl.global_table) {
+    sp.table = csa::kTableGlobal;
     sp.g_flag = reinterpret_cast<const int32_t*>(ws);
     sp.g_off = reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + kHeaderBytes);
+  } else if (cu_host && p.S <= csa::kArgSegments) {
+    sp.table = csa::kTableArgs;
+    int32_t off = 0;
+    for (int32_t s = 0; s <= p.S; ++s) {
+      sp.arg_cu[s] = cu_host[s];
+      sp.arg_off[s] = off;
+      if (s < p.S) off += (cu_host[s + 1] - cu_host[s]) / p.ratio;
+    }
   }
   return sp;
 }
@@ -253,7 +280,7 @@ csa_status_t after_launch(const char* what) {
 csa_status_t launch_scan_if_needed(const Problem& p, const Plan& pl, const int32_t* cu, void* ws,
                                    hipStream_t stream) {
   if (!pl.global_table) return CSA_STATUS_SUCCESS;
-  const csa::SegParams sp = seg_params(p, pl, cu, ws);
+  const csa::SegParams sp = seg_params(p, pl, cu, nullptr, ws);
   int32_t* flag = reinterpret_cast<int32_t*>(ws);
   int32_t* off = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + kHeaderBytes);
   if (!csa::launch_seg_scan(p.ratio, sp, off, flag, stream))
@@ -285,12 +312,12 @@ csa_status_t check_bwd_args(const Problem& pr, const Plan& pl, const void* kv, c
 }
 
 csa_status_t launch_bwd_grads(const Problem& pr, const Plan& pl, const void* kv, const void* score,
-                              const float* ape, const int32_t* cu, const void* dout, void* dkv, void* dscore,
-                              void* workspace, hipStream_t stream) {
+                              const float* ape, const int32_t* cu, const int32_t* cu_host, const void* dout,
+                              void* dkv, void* dscore, void* workspace, hipStream_t stream) {
   csa_status_t st = launch_scan_if_needed(pr, pl, cu, workspace, stream);
   if (st) return st;
   csa::BwdParams bp{};
-  bp.seg = seg_params(pr, pl, cu, workspace);
+  bp.seg = seg_params(pr, pl, cu, cu_host, workspace);
   bp.kv = static_cast<const uint16_t*>(kv);
   bp.score = static_cast<const uint16_t*>(score);
   bp.ape = ape;
@@ -382,12 +409,13 @@ csa_status_t csa_compressor_bwd_workspace_size(int32_t ratio, int32_t coff, int3
 }
 
 csa_status_t csa_compressor_fwd(const void* kv, const void* score, const float* ape, const int32_t* cu,
-                                int32_t S, int64_t total_tokens, int64_t total_comp, int32_t ratio,
-                                int32_t coff, int32_t head_dim, void* out, void* workspace,
+                                const int32_t* cu_host, int32_t S, int64_t total_tokens, int64_t total_comp,
+                                int32_t ratio, int32_t coff, int32_t head_dim, void* out, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
   const Problem pr{ratio, coff, head_dim, S, total_tokens, total_comp};
   csa_status_t st = check_problem(pr);
   if (st) return st;
+  if ((st = check_host_cu(pr, cu_host))) return st;
   if (pr.N == 0) return ok();  // no output rows: nothing to do
   if ((st = check_ptr(kv, "kv")) || (st = check_ptr(score, "score")) || (st = check_ptr(ape, "ape")) ||
       (st = check_ptr(out, "out")))
@@ -402,7 +430,7 @@ csa_status_t csa_compressor_fwd(const void* kv, const void* score, const float* 
 
   if ((st = launch_scan_if_needed(pr, pl, cu, workspace, stream))) return st;
   csa::FwdParams fp{};
-  fp.seg = seg_params(pr, pl, cu, workspace);
+  fp.seg = seg_params(pr, pl, cu, cu_host, workspace);
   fp.kv = static_cast<const uint16_t*>(kv);
   fp.score = static_cast<const uint16_t*>(score);
   fp.ape = ape;
@@ -416,15 +444,16 @@ csa_status_t csa_compressor_fwd(const void* kv, const void* score, const float* 
 }
 
 csa_status_t csa_compressor_bwd_grads(const void* kv, const void* score, const float* ape, const int32_t* cu,
-                                      int32_t S, int64_t total_tokens, int64_t total_comp, int32_t ratio,
-                                      int32_t coff, int32_t head_dim, const void* dout, void* dkv, void* dscore,
-                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                                      const int32_t* cu_host, int32_t S, int64_t total_tokens, int64_t total_comp,
+                                      int32_t ratio, int32_t coff, int32_t head_dim, const void* dout, void* dkv,
+                                      void* dscore, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const Problem pr{ratio, coff, head_dim, S, total_tokens, total_comp};
   csa_status_t st = check_problem(pr);
   if (st) return st;
+  if ((st = check_host_cu(pr, cu_host))) return st;
   const Plan pl = make_plan(pr);
   if ((st = check_bwd_args(pr, pl, kv, score, ape, cu, dout, dkv, dscore, workspace, workspace_bytes))) return st;
-  return launch_bwd_grads(pr, pl, kv, score, ape, cu, dout, dkv, dscore, workspace, stream);
+  return launch_bwd_grads(pr, pl, kv, score, ape, cu, cu_host, dout, dkv, dscore, workspace, stream);
 }
 
 csa_status_t csa_compressor_bwd_dape_reduce(int32_t ratio, int32_t coff, int32_t head_dim, int32_t S,
@@ -443,18 +472,19 @@ csa_status_t csa_compressor_bwd_dape_reduce(int32_t ratio, int32_t coff, int32_t
 }
 
 csa_status_t csa_compressor_bwd(const void* kv, const void* score, const float* ape, const int32_t* cu,
-                                int32_t S, int64_t total_tokens, int64_t total_comp, int32_t ratio, int32_t coff,
-                                int32_t head_dim, const void* dout, void* dkv, void* dscore, float* dape,
-                                int32_t deterministic, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+                                const int32_t* cu_host, int32_t S, int64_t total_tokens, int64_t total_comp,
+                                int32_t ratio, int32_t coff, int32_t head_dim, const void* dout, void* dkv,
+                                void* dscore, float* dape, int32_t deterministic, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
   (void)deterministic;  // this build always reduces dAPE in a fixed order
   const Problem pr{ratio, coff, head_dim, S, total_tokens, total_comp};
   csa_status_t st = check_problem(pr);
   if (st) return st;
+  if ((st = check_host_cu(pr, cu_host))) return st;
   const Plan pl = make_plan(pr);
   if ((st = check_bwd_args(pr, pl, kv, score, ape, cu, dout, dkv, dscore, workspace, workspace_bytes))) return st;
   if ((st = check_ptr(dape, "dape"))) return st;
-  if ((st = launch_bwd_grads(pr, pl, kv, score, ape, cu, dout, dkv, dscore, workspace, stream))) return st;
+  if ((st = launch_bwd_grads(pr, pl, kv, score, ape, cu, cu_host, dout, dkv, dscore, workspace, stream))) return st;
   return launch_reduce(pr, pl, dape, workspace, stream);
 }
 

@@ -35,7 +35,10 @@
 //     sums the partial rows in a fixed order.  Deterministic.
 //   * The cu_seqlens -> output-block offset scan runs in each workgroup's
 //     prologue (LDS) for up to kMaxLdsSegments segments; larger packs use a
-//     one-workgroup scan kernel writing the offsets to the workspace.
+//     one-workgroup scan kernel writing the offsets to the workspace; small
+//     packs whose host copy of cu_seqlens the caller passes get the table in
+//     the kernel arguments (no dependent global load before the first data
+//     load).
 //   * Floating point follows one fixed fp32 evaluation order (see
 //     include/csa.h); the library is compiled with -ffp-contract=off so only
 //     the explicit fmas below are fused.
@@ -296,18 +299,37 @@ __device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t& excl
 }
 
 // Returns true (uniformly across the block) iff cu is a valid pack for
-// (S, T_cap, N).  GT = false: the table is built in LDS (layout: int64
-// scratch[NT/64], cu[S+1], off[S+1]) and every later lookup is an LDS read.
-// GT = true: the table was built in the workspace by seg_scan_kernel.  The
-// location is a template parameter so lookups compile to ds_read (LDS) or
-// global_load (workspace), never to flat loads, which would make every
-// lookup wait for all outstanding buffer loads.
-template <int R, int NT, bool GT>
+// (S, T_cap, N).  The table location is a template parameter so lookups
+// compile to ds_read (LDS) or global_load (workspace), never to flat loads,
+// which would make every lookup wait for all outstanding buffer loads.
+//   kTableLds:    built here in LDS from the device cu_seqlens (validated);
+//                 LDS layout: int64 scratch[NT/64], cu[S+1], off[S+1].
+//   kTableArgs:   copied to the same LDS layout from the kernel arguments
+//                 (validated on the host): no global load before the first
+//                 data load.
+//   kTableGlobal: built in the workspace by seg_scan_kernel.
+template <int R, int NT, int TBL>
 __device__ bool load_segment_table(const SegParams& sp, int32_t* lds, SegTable& t) {
-  if constexpr (GT) {
+  if constexpr (TBL == kTableGlobal) {
     t.cu = sp.cu;
     t.off = sp.g_off;
     return __builtin_nontemporal_load(sp.g_flag) == 1;
+  } else if constexpr (TBL == kTableArgs) {
+    int32_t* s_cu = lds + 2 * (NT / 64);
+    int32_t* s_off = s_cu + (sp.S + 1);
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int i = 0; i <= kArgSegments; ++i) {
+        if (i <= sp.S) {
+          s_cu[i] = sp.arg_cu[i];
+          s_off[i] = sp.arg_off[i];
+        }
+      }
+    }
+    __syncthreads();
+    t.cu = s_cu;
+    t.off = s_off;
+    return true;
   } else {
     const int S = sp.S;
     int64_t* s_wave = reinterpret_cast<int64_t*>(lds);
@@ -463,11 +485,11 @@ __device__ __forceinline__ Pack<C> fwd_window(const Window<R, CO, C, BWD>& w, co
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
-template <int R, int CO, int C, int NT, bool GT>
+template <int R, int CO, int C, int NT, int TBL>
 __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
   extern __shared__ int32_t lds[];
   SegTable tab;
-  if (!load_segment_table<R, NT, GT>(p.seg, lds, tab)) return;
+  if (!load_segment_table<R, NT, TBL>(p.seg, lds, tab)) return;
 
   const uint32_t d = p.head_dim, W = CO * d;
   const uint32_t lgG = p.log2_chunks, G = 1u << lgG;
@@ -550,12 +572,12 @@ __device__ void zero_sweep(const BwdParams& p, const SegTable& tab) {
   zero_range(rdsc, b0, b1, zid * NT + threadIdx.x, nz * NT);
 }
 
-template <int R, int CO, int C, int NT, bool GT>
+template <int R, int CO, int C, int NT, int TBL>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   extern __shared__ int32_t lds[];
   SegTable tab;
-  const bool valid = load_segment_table<R, NT, GT>(p.seg, lds, tab);
-  if (!GT && blockIdx.x == 0 && threadIdx.x == 0)
+  const bool valid = load_segment_table<R, NT, TBL>(p.seg, lds, tab);
+  if (TBL != kTableGlobal && blockIdx.x == 0 && threadIdx.x == 0)
     __builtin_nontemporal_store(valid ? 1 : 0, p.ws_flag);
   if (!valid) return;
   if (blockIdx.x >= p.main_wgs) {
@@ -858,20 +880,24 @@ __global__ __launch_bounds__(kScanNT) void seg_scan_kernel(SegParams sp, int32_t
 // ---------------------------------------------------------------------------
 template <int R, int CO, int C>
 static void launch_fwd_rcc(const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
-  if (p.seg.global_table)
-    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, true>), dim3(sh.grid), dim3(kFwdThreads), sh.lds_bytes,
-                       st, p);
+  const dim3 grid(sh.grid), block(kFwdThreads);
+  if (p.seg.table == kTableGlobal)
+    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableGlobal>), grid, block, sh.lds_bytes, st, p);
+  else if (p.seg.table == kTableArgs)
+    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableArgs>), grid, block, sh.lds_bytes, st, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, false>), dim3(sh.grid), dim3(kFwdThreads), sh.lds_bytes,
-                       st, p);
+    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableLds>), grid, block, sh.lds_bytes, st, p);
 }
 
 template <int R, int CO, int C, int NT>
 static void launch_bwd_rccn(const BwdParams& p, const LaunchShape& sh, hipStream_t st) {
-  if (p.seg.global_table)
-    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, true>), dim3(sh.grid), dim3(NT), sh.lds_bytes, st, p);
+  const dim3 grid(sh.grid), block(NT);
+  if (p.seg.table == kTableGlobal)
+    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableGlobal>), grid, block, sh.lds_bytes, st, p);
+  else if (p.seg.table == kTableArgs)
+    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableArgs>), grid, block, sh.lds_bytes, st, p);
   else
-    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, false>), dim3(sh.grid), dim3(NT), sh.lds_bytes, st, p);
+    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableLds>), grid, block, sh.lds_bytes, st, p);
 }
 
 template <int R, int CO>

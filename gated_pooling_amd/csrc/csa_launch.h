@@ -12,6 +12,16 @@ constexpr int kFwdThreads = 256;
 // Packs with more segments than this build their offset table with a
 // separate scan kernel into the workspace instead of in each workgroup's LDS.
 constexpr int kMaxLdsSegments = 2048;
+// Packs with at most this many segments whose host copy of cu_seqlens is
+// given take cu and the block offsets as kernel arguments.
+constexpr int kArgSegments = 32;
+
+// Where the kernels find the segment table.
+enum TableKind : int32_t {
+  kTableLds = 0,     // built per workgroup in LDS from the device cu_seqlens
+  kTableGlobal = 1,  // built in the workspace by seg_scan_kernel (large packs)
+  kTableArgs = 2,    // passed in the kernel arguments (host copy, small packs)
+};
 
 struct SegParams {
   const int32_t* cu;      // device cu_seqlens [S + 1]
@@ -20,7 +30,9 @@ struct SegParams {
   int64_t T_cap;          // total_tokens (row capacity)
   int64_t N;              // total_comp as given by the caller
   int32_t S;
-  int32_t global_table;   // 1: use g_off / g_flag
+  int32_t table;          // TableKind
+  int32_t arg_cu[kArgSegments + 1];   // kTableArgs: cu_seqlens
+  int32_t arg_off[kArgSegments + 1];  // kTableArgs: output-block offsets
 };
 
 struct FwdParams {

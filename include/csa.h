@@ -51,12 +51,20 @@
  *     on the device and, if it does not hold, touch nothing but the
  *     workspace (outputs are left as they were).
  *   - total_comp is supplied by the caller (see csa_compressor_total_comp).
+ *   - cu_seqlens_host (optional, may be NULL): a HOST copy of the same
+ *     cu_seqlens.  When given it is validated on the host (cu[0] == 0,
+ *     non-decreasing, cu[S] <= total_tokens, sum floor(L_s/ratio) ==
+ *     total_comp; INVALID_VALUE otherwise) and, for packs of up to 32
+ *     segments, the kernels take the segment table from their arguments and
+ *     do not read the device cu_seqlens at all (the two copies must agree).
+ *     Pass NULL when the device copy may change without the host knowing
+ *     (e.g. a captured graph replayed with new cu_seqlens).
  *   - Work is enqueued on `stream` and is asynchronous; launch failures are
  *     returned as CSA_STATUS_LAUNCH_FAILED.
  *   - Validation is host-only and happens before any HIP call, so every
  *     rejection path works without a GPU.
- *   - Thread-safe: no global mutable state besides a per-device cache of the
- *     compute-unit count and the thread-local error text.
+ *   - Thread-safe: no global mutable state besides the thread-local error
+ *     text and tuning knobs read once from the environment.
  */
 #ifndef CSA_H_
 #define CSA_H_
@@ -84,7 +92,7 @@ typedef enum csa_status {
     CSA_STATUS_WORKSPACE_TOO_SMALL = 3,
     /* a kernel launch failed (hipGetLastError after the launch) */
     CSA_STATUS_LAUNCH_FAILED = 4,
-    /* the current device could not be queried */
+    /* reserved: the current device could not be queried */
     CSA_STATUS_DEVICE_ERROR = 5
 } csa_status_t;
 
@@ -114,8 +122,8 @@ csa_status_t csa_compressor_check_support(int32_t ratio, int32_t coff, int32_t h
                                           int32_t num_segments, int64_t total_tokens,
                                           int64_t total_comp);
 
-/* Workspace bytes the forward / backward need on the CURRENT device for this
- * problem (0 is possible).  The workspace is device memory, 16-byte aligned,
+/* Workspace bytes the forward / backward need for this problem (0 is
+ * possible; the size depends on the problem, not on the device).  The workspace is device memory, 16-byte aligned,
  * caller-owned, uninitialized on entry, and may be reused across calls that
  * are stream-ordered; two calls running concurrently need two workspaces. */
 csa_status_t csa_compressor_fwd_workspace_size(int32_t ratio, int32_t coff, int32_t head_dim,
@@ -129,11 +137,12 @@ csa_status_t csa_compressor_bwd_workspace_size(int32_t ratio, int32_t coff, int3
  *   kv, score  bf16 [total_tokens, coff*head_dim]   (device, read)
  *   ape        fp32 [ratio, coff*head_dim]           (device, read)
  *   cu_seqlens int32 [num_segments + 1]              (device, read)
+ *   cu_seqlens_host int32 [num_segments + 1]         (host, optional)
  *   out        bf16 [total_comp, head_dim]           (device, fully written)
  * total_comp == 0 enqueues nothing. */
 csa_status_t csa_compressor_fwd(const void* kv, const void* score, const float* ape,
-                                const int32_t* cu_seqlens, int32_t num_segments,
-                                int64_t total_tokens, int64_t total_comp,
+                                const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                int32_t num_segments, int64_t total_tokens, int64_t total_comp,
                                 int32_t ratio, int32_t coff, int32_t head_dim,
                                 void* out, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
@@ -156,8 +165,8 @@ csa_status_t csa_compressor_fwd(const void* kv, const void* score, const float* 
  * (0 would permit an unordered reduction) and does not change the result of
  * this build.  total_comp == 0 still writes all zeros to dkv/dscore/dape. */
 csa_status_t csa_compressor_bwd(const void* kv, const void* score, const float* ape,
-                                const int32_t* cu_seqlens, int32_t num_segments,
-                                int64_t total_tokens, int64_t total_comp,
+                                const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                int32_t num_segments, int64_t total_tokens, int64_t total_comp,
                                 int32_t ratio, int32_t coff, int32_t head_dim,
                                 const void* dout, void* dkv, void* dscore, float* dape,
                                 int32_t deterministic, void* workspace, size_t workspace_bytes,
@@ -173,8 +182,8 @@ csa_status_t csa_compressor_bwd(const void* kv, const void* score, const float* 
  * bwd_dape_reduce must run after bwd_grads of the same problem on the same
  * workspace, with nothing writing the workspace in between. */
 csa_status_t csa_compressor_bwd_grads(const void* kv, const void* score, const float* ape,
-                                      const int32_t* cu_seqlens, int32_t num_segments,
-                                      int64_t total_tokens, int64_t total_comp,
+                                      const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                      int32_t num_segments, int64_t total_tokens, int64_t total_comp,
                                       int32_t ratio, int32_t coff, int32_t head_dim,
                                       const void* dout, void* dkv, void* dscore,
                                       void* workspace, size_t workspace_bytes,

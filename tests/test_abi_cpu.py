@@ -135,15 +135,16 @@ def test_workspace_sizes():
         G.csa_compressor_bwd_workspace_size(3, 2, 16, 2, 64, 15)
 
 
-def _fwd(kv=A, score=A, ape=A, cu=B, S=2, T=64, N=15, r=4, c=2, d=16, out=A, ws=NULL, wsb=0):
-    return G.lib().csa_compressor_fwd(kv, score, ape, cu, S, T, N, r, c, d, out, ws, wsb, NULL)
+def _fwd(kv=A, score=A, ape=A, cu=B, S=2, T=64, N=15, r=4, c=2, d=16, out=A, ws=NULL, wsb=0, cu_host=NULL):
+    return G.lib().csa_compressor_fwd(kv, score, ape, cu, cu_host, S, T, N, r, c, d, out, ws, wsb, NULL)
 
 
 def _bwd(kv=A, score=A, ape=A, cu=B, S=2, T=64, N=15, r=4, c=2, d=16, dout=A, dkv=A, dsc=A, dape=A,
-         ws=A, wsb=None):
+         ws=A, wsb=None, cu_host=NULL):
     if wsb is None:
         wsb = G.csa_compressor_bwd_workspace_size(r, c, d, max(S, 0), max(T, 0), max(N, 0)) if min(S, T, N) >= 0 else 0
-    return G.lib().csa_compressor_bwd(kv, score, ape, cu, S, T, N, r, c, d, dout, dkv, dsc, dape, 1, ws, wsb, NULL)
+    return G.lib().csa_compressor_bwd(kv, score, ape, cu, cu_host, S, T, N, r, c, d, dout, dkv, dsc, dape, 1, ws, wsb,
+                                      NULL)
 
 
 def test_fwd_rejections_happen_before_any_launch():
@@ -182,10 +183,22 @@ def test_bwd_rejections_happen_before_any_launch():
     need = G.csa_compressor_bwd_workspace_size(4, 2, 16, 2, 64, 15)
     assert _bwd(wsb=need - 1) == WS
     L = G.lib()
-    assert L.csa_compressor_bwd_grads(A, A, A, B, 2, 64, 15, 4, 2, 16, A, A, A, A, need - 1, NULL) == WS
+    assert L.csa_compressor_bwd_grads(A, A, A, B, NULL, 2, 64, 15, 4, 2, 16, A, A, A, A, need - 1, NULL) == WS
     assert L.csa_compressor_bwd_dape_reduce(4, 2, 16, 2, 64, 15, NULL, A, need, NULL) == INV
     assert L.csa_compressor_bwd_dape_reduce(4, 2, 16, 2, 64, 15, A, A, need - 1, NULL) == WS
     assert L.csa_compressor_bwd_dape_reduce(3, 2, 16, 2, 64, 15, A, A, need, NULL) == NS
+
+
+def test_host_cu_is_validated_before_any_launch():
+    INV = G.CSA_STATUS_INVALID_VALUE
+    bad_total = G.host_cu([0, 37, 60])      # 9 + 5 = 14 rows, not 15
+    bad_start = G.host_cu([1, 37, 64])
+    bad_order = G.host_cu([0, 40, 37])
+    past_end = G.host_cu([0, 37, 68])
+    for h in (bad_total, bad_start, bad_order, past_end):
+        assert _fwd(cu_host=h) == INV
+        assert _bwd(cu_host=h) == INV
+    assert "cu_seqlens_host" in G.csa_last_error()
 
 
 def test_tensor_binding_validates_on_host():

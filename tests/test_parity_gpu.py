@@ -38,14 +38,18 @@ def bf16_nan(shape, device):
     return torch.full(shape, NAN_BF16, dtype=torch.int16, device=device).view(torch.bfloat16)
 
 
-def run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N, stages=False):
+def run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N, stages=False, host=True):
     """Forward and backward on the GPU with NaN-prefilled outputs; returns
-    numpy (out bits, dkv bits, dscore bits, dape f32)."""
+    numpy (out bits, dkv bits, dscore bits, dape f32).  host=True also passes
+    the host copy of cu_seqlens (small packs then take the segment table from
+    the kernel arguments); host=False makes the kernels build it from the
+    device copy."""
     W = c * d
     cu_d = torch.tensor(cu, dtype=torch.int32, device=dev)
+    cu_h = list(cu) if host else None
     kv_d, sc_d, ape_d, dout_d = kv.to(dev), sc.to(dev), ape.to(dev), dout.to(dev)
     out = bf16_nan((N, d), dev)
-    G.compressor_fwd(kv_d, sc_d, ape_d, cu_d, r, c, N, out=out)
+    G.compressor_fwd(kv_d, sc_d, ape_d, cu_d, r, c, N, out=out, cu_seqlens_host=cu_h)
     dkv, dsc = bf16_nan((T, W), dev), bf16_nan((T, W), dev)
     dape = torch.full((r, W), float("nan"), dtype=torch.float32, device=dev)
     if stages:
@@ -53,11 +57,12 @@ def run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N, stages=False):
         ws = G.workspace(nbytes, dev)
         P = lambda t: t.data_ptr()  # noqa: E731
         s = torch.cuda.current_stream().cuda_stream
-        G.csa_compressor_bwd_grads(P(kv_d), P(sc_d), P(ape_d), P(cu_d), len(cu) - 1, T, N, r, c, d, P(dout_d),
-                                   P(dkv), P(dsc), P(ws), ws.numel(), s)
+        G.csa_compressor_bwd_grads(P(kv_d), P(sc_d), P(ape_d), P(cu_d), G.host_cu(cu_h), len(cu) - 1, T, N, r, c,
+                                   d, P(dout_d), P(dkv), P(dsc), P(ws), ws.numel(), s)
         G.csa_compressor_bwd_dape_reduce(r, c, d, len(cu) - 1, T, N, P(dape), P(ws), ws.numel(), s)
     else:
-        G.compressor_bwd(kv_d, sc_d, ape_d, cu_d, r, c, N, dout_d, dkv=dkv, dscore=dsc, dape=dape)
+        G.compressor_bwd(kv_d, sc_d, ape_d, cu_d, r, c, N, dout_d, dkv=dkv, dscore=dsc, dape=dape,
+                         cu_seqlens_host=cu_h)
     torch.cuda.synchronize()
     return (inputs.bits(out.cpu()), inputs.bits(dkv.cpu()), inputs.bits(dsc.cpu()), dape.cpu().numpy())
 
@@ -106,14 +111,15 @@ def check_against_oracle(cu, T, r, c, d, kv, sc, ape, dout, got):
 # every workload at its full size
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("host", [True, False], ids=["args_table", "device_table"])
 @pytest.mark.parametrize("name", list(inputs.WORKLOADS))
-def test_workload_parity(dev, name):
+def test_workload_parity(dev, name, host):
     wl = inputs.WORKLOADS[name]
     cu, T, r, c, d = list(wl.cu_seqlens), wl.total_tokens, wl.ratio, wl.coff, wl.head_dim
     N = G.csa_compressor_total_comp(cu, r)
     assert N == oracle.total_comp(cu, r)
     kv, sc, ape, dout = inputs.make_tensors(wl, N)
-    got = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N)
+    got = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N, host=host)
     check_against_oracle(cu, T, r, c, d, kv, sc, ape, dout, got)
 
 
@@ -124,8 +130,9 @@ def test_stage_split_equals_full_backward(dev):
     kv, sc, ape, dout = inputs.make_tensors(wl, N)
     a = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N)
     b = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N, stages=True)
-    for x, y in zip(a, b):
-        assert np.array_equal(x, y)
+    c_ = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N, stages=True, host=False)
+    for x, y, z in zip(a, b, c_):
+        assert np.array_equal(x, y) and np.array_equal(x, z)
 
 
 @pytest.mark.parametrize("name", ["3x8192_d512_r4_c2", "ragged_d128_r4_c1", "ragged_d128_r4_c2",
@@ -252,7 +259,7 @@ def test_invalid_device_cu_seqlens_touches_nothing(dev):
     kv, sc, ape, dout = inputs.make_tensors(wl, N)
     bad = torch.tensor([0, 37, 60], dtype=torch.int32, device=dev)  # implies 9 + 5 = 14 blocks
     out = bf16_nan((N, 16), dev)
-    G.compressor_fwd(kv.to(dev), sc.to(dev), ape.to(dev), bad, 4, 2, N, out=out)
+    G.compressor_fwd(kv.to(dev), sc.to(dev), ape.to(dev), bad, 4, 2, N, out=out)  # no host copy: device check
     dkv, dsc = bf16_nan((64, 32), dev), bf16_nan((64, 32), dev)
     dape = torch.full((4, 32), float("nan"), device=dev)
     G.compressor_bwd(kv.to(dev), sc.to(dev), ape.to(dev), bad, 4, 2, N, dout.to(dev), dkv=dkv, dscore=dsc, dape=dape)
