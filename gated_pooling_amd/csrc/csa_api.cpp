@@ -57,9 +57,9 @@ struct Tuning {
   int fwd_cols = 4;
   int fwd_max_wgs = 2048;
   int bwd_cols = 2;
-  int bwd_threads = 1024;
-  int bwd_max_wgs = 256;
-  int bwd_slice_bytes = 128;
+  int bwd_threads = 256;
+  int bwd_max_wgs = 768;
+  int bwd_slice_bytes = 512;
 };
 
 int env_int(const char* name, int dflt, const int* allowed, int n_allowed, int lo, int hi) {

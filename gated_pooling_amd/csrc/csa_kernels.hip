@@ -74,32 +74,40 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int C>
+// Cache policy bits of buffer instructions: kAuxStream marks data that is
+// touched once (kv/score reads, dkv/dscore writes) as non-temporal.  Build
+// knob CSA_STREAM_HINT (0 disables the hint).
+#ifndef CSA_STREAM_HINT
+#define CSA_STREAM_HINT 2
+#endif
+constexpr int kAuxStream = CSA_STREAM_HINT;
+
+template <int C, int AUX = kAuxStream>
 __device__ __forceinline__ Pack<C> load_pack(rsrc_t r, uint32_t byte_off) {
   Pack<C> p;
   if constexpr (C == 8) {
-    u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+    u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, AUX);
     p.w[0] = v.x; p.w[1] = v.y; p.w[2] = v.z; p.w[3] = v.w;
   } else if constexpr (C == 4) {
-    u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
+    u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, AUX);
     p.w[0] = v.x; p.w[1] = v.y;
   } else {
     static_assert(C == 2, "C must be 2, 4 or 8");
-    p.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
+    p.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, AUX);
   }
   return p;
 }
 
-template <int C>
+template <int C, int AUX = kAuxStream>
 __device__ __forceinline__ void store_pack(rsrc_t r, uint32_t byte_off, const Pack<C>& p) {
   if constexpr (C == 8) {
     u32x4 v = {p.w[0], p.w[1], p.w[2], p.w[3]};
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, AUX);
   } else if constexpr (C == 4) {
     u32x2 v = {p.w[0], p.w[1]};
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, AUX);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b32(p.w[0], r, byte_off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(p.w[0], r, byte_off, 0, AUX);
   }
 }
 
@@ -813,7 +821,9 @@ __global__ __launch_bounds__(kReduceNT) void dape_reduce_kernel(ReduceParams p) 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t col = blockIdx.x * 64 + lane;
   const uint32_t cols = p.cols, rows = p.rows;
-  if (__builtin_nontemporal_load(p.ws_flag) != 1) return;  // bad cu_seqlens: leave dape untouched
+  // the validity flag is loaded alongside the partials and checked before
+  // anything is stored (bad cu_seqlens: dape is left untouched)
+  const int32_t flag = __builtin_nontemporal_load(p.ws_flag);
   const rsrc_t rpart = make_rsrc(p.partials, rows * cols * 4u);
   float s = 0.0f;
   if (col < cols) {
@@ -830,7 +840,7 @@ __global__ __launch_bounds__(kReduceNT) void dape_reduce_kernel(ReduceParams p) 
   }
   part[wave][lane] = s;
   __syncthreads();
-  if (wave == 0 && col < cols) {
+  if (wave == 0 && col < cols && flag == 1) {
     float t = part[0][lane];
 #pragma unroll
     for (int w = 1; w < kReduceWaves; ++w) t = t + part[w][lane];
