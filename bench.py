@@ -29,6 +29,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -89,6 +90,65 @@ def load_traffic(kernel, workload):
     return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
+ROLE_OF_KERNEL = (("fwd_kernel", "fwd"), ("bwd_kernel", "bwd_grads"), ("dape_reduce_kernel", "dape_reduce"))
+COPY_BYTES = 512 * 2 ** 20  # the context copy below moves 512 MiB each way
+
+
+def summarize_counters(fetch_dir, write_dir, workload):
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE; counters in KiB per dispatch) into HBM bytes per launch for
+    each kernel of the path, and store them in profiles/hbm_counters.json
+    keyed by the sha256 of the kernel sources.  Each counter is scaled by what
+    it reads for the 512 MiB device-to-device copy that the same run makes
+    (known to fetch and to write exactly 512 MiB per dispatch)."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for row in csv.DictReader(open(f)):
+                if row["Counter_Name"] != counter:
+                    continue
+                name = row["Kernel_Name"]
+                role = next((r for k, r in ROLE_OF_KERNEL if re.search(r"\b" + k + r"[<(]", name)), None)
+                if role is None and "copy" in name.lower():
+                    role = "copy"
+                if role is not None:
+                    vals.setdefault(role, []).append(float(row["Counter_Value"]) * 1024.0)
+        if "copy" in vals:  # keep the 512 MiB copies, not the small staging copies of the inputs
+            top = max(vals["copy"])
+            vals["copy"] = [v for v in vals["copy"] if v >= 0.25 * top]
+        return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+
+    fetch, nf = per_kernel(fetch_dir, "FETCH_SIZE")
+    write, nw = per_kernel(write_dir, "WRITE_SIZE")
+    if "copy" not in fetch or "copy" not in write:
+        raise SystemExit("summarize_counters: no copy kernel in the counter runs")
+    ff, wf = COPY_BYTES / fetch["copy"], COPY_BYTES / write["copy"]
+    kern = {}
+    for _, role in ROLE_OF_KERNEL:
+        if role in fetch and role in write:
+            kern[role] = {"fetch_bytes": round(fetch[role] * ff), "write_bytes": round(write[role] * wf),
+                          "hbm_bytes_per_launch": round(fetch[role] * ff + write[role] * wf),
+                          "dispatches": [nf[role], nw[role]]}
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    if rec.get("sources_sha256") != sources_digest():
+        rec = {}
+    rec["sources_sha256"] = sources_digest()
+    rec["scale"] = {"FETCH_SIZE": round(ff, 4), "WRITE_SIZE": round(wf, 4),
+                    "copy_counter_bytes": {"FETCH_SIZE": round(fetch["copy"]), "WRITE_SIZE": round(write["copy"])}}
+    rec.setdefault("kernels", {})[workload] = kern
+    with open(COUNTERS, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec["kernels"][workload]))
+
+
 def cpu_baseline(wl, N, kv, sc, ape, dout, budget_s):
     """Time the CPU oracle (fp32 evaluation order, OpenMP over windows) on the
     same pack: forward + backward, repeated until about budget_s seconds."""
@@ -125,7 +185,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-warm", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/hbm_counters.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        from gated_pooling_amd import inputs
+        summarize_counters(*args.summarize_counters, args.workload or inputs.HEADLINE)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -186,28 +253,36 @@ def main():
 
     nsets = len(sets)
 
-    def run_steps(K, events=None):
+    def run_steps(K):
         """K steps in groups of nsets: the group's forwards, then its backwards."""
         done = 0
         while done < K:
             grp = list(range(min(nsets, K - done)))
             for j in grp:
-                if events is not None:
-                    events["fwd"][done + j][0].record(stream)
                 fwd(sets[j])
-                if events is not None:
-                    events["fwd"][done + j][1].record(stream)
             for j in grp:
-                if events is not None:
-                    events["bwd_grads"][done + j][0].record(stream)
                 grads(sets[j])
-                if events is not None:
-                    events["bwd_grads"][done + j][1].record(stream)
-                    events["dape_reduce"][done + j][0].record(stream)
                 reduce(sets[j])
-                if events is not None:
-                    events["dape_reduce"][done + j][1].record(stream)
             done += len(grp)
+
+    def run_steps_timed(K):
+        """The same K steps with each kernel's launches of a group issued back
+        to back between two HIP events on the launch stream: per-kernel time =
+        the group's event interval / launches, which includes no event or
+        host overhead between the launches it averages."""
+        spans = {"fwd": [], "bwd_grads": [], "dape_reduce": []}
+        done = 0
+        while done < K:
+            grp = list(range(min(nsets, K - done)))
+            for name, fn in (("fwd", fwd), ("bwd_grads", grads), ("dape_reduce", reduce)):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for j in grp:
+                    fn(sets[j])
+                b.record(stream)
+                spans[name].append((a, b, len(grp)))
+            done += len(grp)
+        return spans
 
     # warm-up, then the timed region: K steps, nothing but the work itself
     run_steps(max(args.warmup, 0))
@@ -224,21 +299,18 @@ def main():
     ms_per_step = wall * 1e3 / K
     gpu_ms_per_step = region[0].elapsed_time(region[1]) / K
 
-    # second timed region, same K steps and cache protocol, with HIP events
-    # on the launch stream around every kernel: per-kernel durations
-    mk = lambda: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]  # noqa: E731
-    events = {"fwd": mk(), "bwd_grads": mk(), "dape_reduce": mk()}
+    # second timed region: the same K steps, per-kernel HIP events
     torch.cuda.synchronize()
-    run_steps(K, events)
+    spans = run_steps_timed(K)
     torch.cuda.synchronize()
 
     abytes = algorithmic_bytes(cu, T, r, c, d, N)
     step_bytes = sum(abytes.values())
     kern = {}
-    for name, evs in events.items():
-        us = [a.elapsed_time(b) * 1e3 for a, b in evs]
-        avg = sum(us) / len(us)
-        kern[name] = {"avg_us": round(avg, 3), "min_us": round(min(us), 3),
+    for name, sp in spans.items():
+        per = [a.elapsed_time(b) * 1e3 / n for a, b, n in sp]
+        avg = sum(a.elapsed_time(b) * 1e3 for a, b, _ in sp) / sum(n for _, _, n in sp)
+        kern[name] = {"avg_us": round(avg, 3), "min_group_avg_us": round(min(per), 3),
                       "algorithmic_bytes": abytes[name],
                       "GBs": round(abytes[name] / (avg * 1e-6) / 1e9, 1)}
     dom = max(kern, key=lambda k: kern[k]["avg_us"])
@@ -247,19 +319,18 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     warm = None
-    if not args.no_warm:
-        wev = {"fwd": [], "bwd_grads": [], "dape_reduce": []}
-        for _ in range(3):
-            fwd(sets[0]); grads(sets[0]); reduce(sets[0])  # noqa: E702
-        for _ in range(20):
-            for name, fn in (("fwd", fwd), ("bwd_grads", grads), ("dape_reduce", reduce)):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
+    if not args.no_warm:  # context: one buffer set over and over (inputs cache-resident)
+        warm = {}
+        for name, fn in (("fwd", fwd), ("bwd_grads", grads), ("dape_reduce", reduce)):
+            for _ in range(3):
                 fn(sets[0])
-                b.record(stream)
-                wev[name].append((a, b))
-        torch.cuda.synchronize()
-        warm = {k: round(sum(a.elapsed_time(b) for a, b in v) * 1e3 / len(v), 3) for k, v in wev.items()}
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ea.record(stream)
+            for _ in range(20):
+                fn(sets[0])
+            eb.record(stream)
+            torch.cuda.synchronize()
+            warm[name] = round(ea.elapsed_time(eb) * 1e3 / 20, 3)
 
     # context: a plain device-to-device copy of 512 MiB (torch's copy kernel)
     src = torch.empty(256 * 2 ** 20, dtype=torch.int16, device=dev)

@@ -54,7 +54,7 @@ csa_status_t ok() {
 }
 
 struct Tuning {
-  int fwd_cols = 4;
+  int fwd_cols = 2;
   int fwd_max_wgs = 2048;
   int bwd_cols = 2;
   int bwd_threads = 256;
