@@ -55,11 +55,12 @@ csa_status_t ok() {
 
 struct Tuning {
   int fwd_cols = 2;
-  int fwd_max_wgs = 2048;
+  int fwd_max_wgs = 1024;
   int bwd_cols = 2;
   int bwd_threads = 256;
-  int bwd_max_wgs = 768;
+  int bwd_max_wgs = 256;
   int bwd_slice_bytes = 512;
+  int uniform = 1;        // wave-uniform row path where a row has >= 64 chunks
 };
 
 int env_int(const char* name, int dflt, const int* allowed, int n_allowed, int lo, int hi) {
@@ -87,6 +88,7 @@ const Tuning& tuning() {
     d.bwd_threads = env_int("CSA_BWD_THREADS", d.bwd_threads, threads, 3, 0, 0);
     d.bwd_max_wgs = env_int("CSA_BWD_MAX_WGS", d.bwd_max_wgs, nullptr, 0, 1, 1 << 16);
     d.bwd_slice_bytes = env_int("CSA_BWD_SLICE_BYTES", d.bwd_slice_bytes, nullptr, 0, 16, 1 << 16);
+    d.uniform = env_int("CSA_UNIFORM", d.uniform, nullptr, 0, 0, 1);
     return d;
   }();
   return t;
@@ -117,8 +119,10 @@ csa_status_t check_problem(const Problem& p) {
                 p.S, (long long)p.T, (long long)p.N);
   const int64_t W = int64_t{p.coff} * p.head_dim;
   const int64_t lim = int64_t{1} << 31;
-  if (p.T * W >= lim)
-    return fail(CSA_STATUS_NOT_SUPPORTED, "total_tokens*coff*head_dim must be below 2^31");
+  // (total_tokens + 1): a masked load's offset, one row past the end, must
+  // still fit in 32 bits
+  if ((p.T + 1) * W >= lim)
+    return fail(CSA_STATUS_NOT_SUPPORTED, "(total_tokens+1)*coff*head_dim must be below 2^31");
   if (p.N * p.head_dim >= lim)
     return fail(CSA_STATUS_NOT_SUPPORTED, "total_comp*head_dim must be below 2^31");
   if (int64_t{p.ratio} * W >= lim)
@@ -134,7 +138,8 @@ csa_status_t check_problem(const Problem& p) {
 
 // Workspace layout: [0, 256) header (int32 validity flag at 0);
 // then, for packs above kMaxLdsSegments, int32 offsets [S + 1];
-// then (backward) fp32 dAPE partials [partial_rows, ratio, W].
+// then (backward) fp32 dAPE partials in column blocks
+// [ceil(ratio*W / kPartBlock)][partial_rows][kPartBlock].
 struct Plan {
   bool global_table;
   uint64_t off_bytes;   // offsets section size
@@ -173,6 +178,7 @@ Plan make_plan(const Problem& p) {
     pl.fwd.grid = static_cast<uint32_t>(wgs);
     pl.fwd.threads = csa::kFwdThreads;
     pl.fwd.cols = C;
+    pl.fwd.uniform = tu.uniform && G >= 64;
     pl.fwd_log2_chunks = log2i(G);
     const uint64_t table_words = pl.global_table ? 0 : 2 * (csa::kFwdThreads / 64) + 2 * uint64_t(p.S + 1);
     pl.fwd.lds_bytes = table_words * 4;
@@ -209,6 +215,7 @@ Plan make_plan(const Problem& p) {
     pl.bwd.grid = static_cast<uint32_t>(main + zero);
     pl.bwd.threads = NT;
     pl.bwd.cols = C;
+    pl.bwd.uniform = tu.uniform && CS >= 64;
     pl.bwd_log2_chunks = log2i(G);
     pl.bwd_log2_slice = log2i(CS);
     pl.bwd_main_wgs = static_cast<uint32_t>(main);
@@ -217,7 +224,8 @@ Plan make_plan(const Problem& p) {
     const uint64_t red_floats = uint64_t(p.coff) * p.ratio * CS * C;
     pl.bwd.lds_bytes = (uint64_t(pl.lds_table_words) + red_floats) * 4;
     pl.partial_offset = kHeaderBytes + pl.off_bytes;
-    pl.ws_bwd = pl.partial_offset + align_up(uint64_t(pl.partial_rows) * p.ratio * W * 4, 256);
+    const uint64_t nblk = (uint64_t(p.ratio) * W + csa::kPartBlock - 1) / csa::kPartBlock;
+    pl.ws_bwd = pl.partial_offset + align_up(nblk * pl.partial_rows * csa::kPartBlock * 4, 256);
   }
   return pl;
 }

@@ -447,6 +447,78 @@ __device__ __forceinline__ void fetch_window(Window<R, CO, C, BWD>& w, uint32_t 
   if constexpr (BWD) w.gd[0] = load_pack<C>(x.rdo, valid ? (n * x.d + x.g * C) * 2u : x.oob_do);
 }
 
+// ---------------------------------------------------------------------------
+// Wave-uniform windows.  When a row has at least 64 chunks, the 64 lanes of a
+// wave work on the same output row, so the row's segment, first token row
+// and flags are computed once per wave on the scalar unit (table entries
+// read at uniform indices), and each load address is the lane's column
+// offset plus a uniform row offset.  Masked loads use a uniform offset at
+// the end of the buffer (the host keeps end + row bytes below 2^32).
+// ---------------------------------------------------------------------------
+template <int TBL>
+struct UTable {
+  const SegParams& sp;   // kTableArgs: entries straight from the kernel arguments
+  const int32_t* cu;     // otherwise: the table in LDS or in the workspace
+  const int32_t* off;
+  __device__ __forceinline__ uint32_t cu_at(int i) const {
+    if constexpr (TBL == kTableArgs) return static_cast<uint32_t>(sp.arg_cu[i]);
+    else return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(cu[i]));
+  }
+  __device__ __forceinline__ uint32_t off_at(int i) const {
+    if constexpr (TBL == kTableArgs) return static_cast<uint32_t>(sp.arg_off[i]);
+    else return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(off[i]));
+  }
+};
+
+struct WinCtxU {
+  int S;
+  uint32_t N, row_bytes, dout_row_bytes;
+  uint32_t oob_io, oob_do;
+  uint32_t lane_own, lane_prev, lane_gd;  // per-lane byte offsets inside a row
+  rsrc_t rkv, rsc, rdo;
+};
+
+// Fills w for output row n (uniform).  s_hint: a segment index <= the row's
+// segment (rows only increase along a lane's walk); updated in place.
+template <int R, int CO, int C, bool BWD, int TBL>
+__device__ __forceinline__ void fetch_window_u(Window<R, CO, C, BWD>& w, uint32_t n, int& s_hint,
+                                               const UTable<TBL>& t, const WinCtxU& x) {
+  const bool valid = n < x.N;
+  uint32_t own = 0, end = 0, b = 0, nb = 0;
+  if (valid) {
+    int lo = s_hint, hi = x.S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (t.off_at(mid) <= n) lo = mid; else hi = mid - 1;
+    }
+    s_hint = lo;
+    const uint32_t o0 = t.off_at(lo);
+    b = n - o0;
+    nb = t.off_at(lo + 1) - o0;
+    own = t.cu_at(lo) + b * R;
+    end = t.cu_at(lo + 1);
+  }
+  w.own = own;
+  w.seg_end = end;
+  w.has_prev = (CO == 2) && valid && b > 0;
+  w.last = valid && (b + 1 == nb);
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const uint32_t o = x.lane_own + (valid ? (own + i) * x.row_bytes : x.oob_io);
+    w.so[i] = load_pack<C>(x.rsc, o);
+    w.vo[i] = load_pack<C>(x.rkv, o);
+  }
+  if constexpr (CO == 2) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const uint32_t o = x.lane_prev + (w.has_prev ? (own - R + i) * x.row_bytes : x.oob_io);
+      w.sp[i] = load_pack<C>(x.rsc, o);
+      w.vp[i] = load_pack<C>(x.rkv, o);
+    }
+  }
+  if constexpr (BWD) w.gd[0] = load_pack<C>(x.rdo, x.lane_gd + (valid ? n * x.dout_row_bytes : x.oob_do));
+}
+
 // Forward of one window: the C output columns packed as bf16.
 template <int R, int CO, int C, bool BWD>
 __device__ __forceinline__ Pack<C> fwd_window(const Window<R, CO, C, BWD>& w, const float (&ape_r)[CO][R][C]) {
@@ -493,11 +565,14 @@ __device__ __forceinline__ Pack<C> fwd_window(const Window<R, CO, C, BWD>& w, co
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
-template <int R, int CO, int C, int NT, int TBL>
+template <int R, int CO, int C, int NT, int TBL, bool UNI>
 __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
   extern __shared__ int32_t lds[];
-  SegTable tab;
-  if (!load_segment_table<R, NT, TBL>(p.seg, lds, tab)) return;
+  SegTable tab{nullptr, nullptr};
+  // the uniform path reads a kernel-argument table directly: no LDS copy
+  if constexpr (!(UNI && TBL == kTableArgs)) {
+    if (!load_segment_table<R, NT, TBL>(p.seg, lds, tab)) return;
+  }
 
   const uint32_t d = p.head_dim, W = CO * d;
   const uint32_t lgG = p.log2_chunks, G = 1u << lgG;
@@ -506,21 +581,11 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
   const uint32_t nstride = (gridDim.x * NT) >> lgG;
   const uint32_t N = static_cast<uint32_t>(p.seg.N);
   uint32_t n = L >> lgG;
+  if constexpr (UNI) n = __builtin_amdgcn_readfirstlane(n);  // G >= 64: one row per wave
   if (n >= N || nstride == 0) return;
 
-  WinCtx x;
-  x.cu = tab.cu;
-  x.off = tab.off;
-  x.S = p.seg.S;
-  x.N = N;
-  x.W = W;
-  x.d = d;
-  x.g = g;
-  x.oob_io = p.io_bytes;
-  x.oob_do = 0;
-  x.rkv = make_rsrc(p.kv, p.io_bytes);
-  x.rsc = make_rsrc(p.score, p.io_bytes);
-  x.rdo = x.rkv;
+  const rsrc_t rkv = make_rsrc(p.kv, p.io_bytes);
+  const rsrc_t rsc = make_rsrc(p.score, p.io_bytes);
   const rsrc_t rape = make_rsrc(p.ape, R * W * 4u);
   const rsrc_t rout = make_rsrc(p.out, N * d * 2u);
 
@@ -531,12 +596,57 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < R; ++i) load_f32<C>(rape, (i * W + h * d + g * C) * 4u, ape_r[h][i]);
 
-  Window<R, CO, C, false> cur, nxt;
-  fetch_window(cur, n, x);
-  for (; n < N; n += nstride) {
-    fetch_window(nxt, n + nstride, x);
-    store_pack<C>(rout, (n * d + g * C) * 2u, fwd_window(cur, ape_r));
-    cur = nxt;
+  if constexpr (UNI) {
+    const UTable<TBL> t{p.seg, tab.cu, tab.off};
+    WinCtxU x;
+    x.S = p.seg.S;
+    x.N = N;
+    x.row_bytes = W * 2u;
+    x.dout_row_bytes = 0;
+    x.oob_io = p.io_bytes;
+    x.oob_do = 0;
+    x.lane_own = ((CO - 1) * d + g * C) * 2u;
+    x.lane_prev = g * C * 2u;
+    x.lane_gd = 0;
+    x.rkv = rkv;
+    x.rsc = rsc;
+    x.rdo = rkv;
+    const uint32_t lane_out = g * C * 2u, out_row = d * 2u;
+    int s_hint = 0;
+    // two windows in flight, alternating roles (no register copies)
+    Window<R, CO, C, false> wa, wb;
+    fetch_window_u(wa, n, s_hint, t, x);
+    for (;;) {
+      fetch_window_u(wb, n + nstride, s_hint, t, x);
+      store_pack<C>(rout, n * out_row + lane_out, fwd_window(wa, ape_r));
+      n += nstride;
+      if (n >= N) break;
+      fetch_window_u(wa, n + nstride, s_hint, t, x);
+      store_pack<C>(rout, n * out_row + lane_out, fwd_window(wb, ape_r));
+      n += nstride;
+      if (n >= N) break;
+    }
+  } else {
+    WinCtx x;
+    x.cu = tab.cu;
+    x.off = tab.off;
+    x.S = p.seg.S;
+    x.N = N;
+    x.W = W;
+    x.d = d;
+    x.g = g;
+    x.oob_io = p.io_bytes;
+    x.oob_do = 0;
+    x.rkv = rkv;
+    x.rsc = rsc;
+    x.rdo = rkv;
+    Window<R, CO, C, false> cur, nxt;
+    fetch_window(cur, n, x);
+    for (; n < N; n += nstride) {
+      fetch_window(nxt, n + nstride, x);
+      store_pack<C>(rout, (n * d + g * C) * 2u, fwd_window(cur, ape_r));
+      cur = nxt;
+    }
   }
 }
 
@@ -580,11 +690,18 @@ __device__ void zero_sweep(const BwdParams& p, const SegTable& tab) {
   zero_range(rdsc, b0, b1, zid * NT + threadIdx.x, nz * NT);
 }
 
-template <int R, int CO, int C, int NT, int TBL>
+template <int R, int CO, int C, int NT, int TBL, bool UNI>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   extern __shared__ int32_t lds[];
-  SegTable tab;
-  const bool valid = load_segment_table<R, NT, TBL>(p.seg, lds, tab);
+  SegTable tab{nullptr, nullptr};
+  bool valid = true;
+  // the uniform path reads a kernel-argument table directly (no LDS copy);
+  // the zero-fill workgroups still walk it from LDS
+  if constexpr (UNI && TBL == kTableArgs) {
+    if (blockIdx.x >= p.main_wgs) load_segment_table<R, NT, TBL>(p.seg, lds, tab);
+  } else {
+    valid = load_segment_table<R, NT, TBL>(p.seg, lds, tab);
+  }
   if (TBL != kTableGlobal && blockIdx.x == 0 && threadIdx.x == 0)
     __builtin_nontemporal_store(valid ? 1 : 0, p.ws_flag);
   if (!valid) return;
@@ -628,27 +745,13 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       for (int k = 0; k < C; ++k) acc_r[h][i][k] = 0.0f;
     }
 
-  WinCtx x;
-  x.cu = tab.cu;
-  x.off = tab.off;
-  x.S = p.seg.S;
-  x.N = N;
-  x.W = W;
-  x.d = d;
-  x.g = g;
-  x.oob_io = p.io_bytes;
-  x.oob_do = N * d * 2u;
-  x.rkv = rkv;
-  x.rsc = rsc;
-  x.rdo = rdo;
+  const uint32_t rowb = W * 2u;
+  const uint32_t lane_prev = g * C * 2u;                 // first-half column chunk
+  const uint32_t lane_own = ((CO - 1) * d + g * C) * 2u;  // own-half column chunk
 
-  const uint32_t col_prev = g * C;
-  const uint32_t col_own = (CO - 1) * d + g * C;
-  uint32_t n = wg_in_slice * rows_per_wg + (threadIdx.x >> lgCS);
-  Window<R, CO, C, true> cur, nxt;
-  fetch_window(cur, n, x);
-  for (; n < N && nstride != 0; n += nstride) {
-    fetch_window(nxt, n + nstride, x);
+  // One window: gradients for its slots, dAPE accumulation, and (segment's
+  // last block) the zeros of the never-read slots next to it.
+  auto body = [&](const Window<R, CO, C, true>& cur) {
     const uint32_t own = cur.own;
     const Pack<C>& gp = cur.gd[0];
     if (CO == 2 && cur.has_prev) {
@@ -695,10 +798,10 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        store_pack<C>(rdkv, ((own - R + i) * W + col_prev) * 2u, gkv[i]);
-        store_pack<C>(rdsc, ((own - R + i) * W + col_prev) * 2u, gsc[i]);
-        store_pack<C>(rdkv, ((own + i) * W + col_own) * 2u, gkv[R + i]);
-        store_pack<C>(rdsc, ((own + i) * W + col_own) * 2u, gsc[R + i]);
+        store_pack<C>(rdkv, (own - R + i) * rowb + lane_prev, gkv[i]);
+        store_pack<C>(rdsc, (own - R + i) * rowb + lane_prev, gsc[i]);
+        store_pack<C>(rdkv, (own + i) * rowb + lane_own, gkv[R + i]);
+        store_pack<C>(rdsc, (own + i) * rowb + lane_own, gsc[R + i]);
       }
     } else {
       Pack<C> gkv[R], gsc[R];
@@ -737,8 +840,8 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        store_pack<C>(rdkv, ((own + i) * W + col_own) * 2u, gkv[i]);
-        store_pack<C>(rdsc, ((own + i) * W + col_own) * 2u, gsc[i]);
+        store_pack<C>(rdkv, (own + i) * rowb + lane_own, gkv[i]);
+        store_pack<C>(rdsc, (own + i) * rowb + lane_own, gsc[i]);
       }
     }
     if (cur.last) {
@@ -749,19 +852,75 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       if (CO == 2) {
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-          store_pack<C>(rdkv, ((own + i) * W + col_prev) * 2u, z);
-          store_pack<C>(rdsc, ((own + i) * W + col_prev) * 2u, z);
+          store_pack<C>(rdkv, (own + i) * rowb + lane_prev, z);
+          store_pack<C>(rdsc, (own + i) * rowb + lane_prev, z);
         }
       }
       for (uint32_t t = own + R; t < cur.seg_end; ++t) {
 #pragma unroll
         for (int h = 0; h < CO; ++h) {
-          store_pack<C>(rdkv, (t * W + h * d + g * C) * 2u, z);
-          store_pack<C>(rdsc, (t * W + h * d + g * C) * 2u, z);
+          store_pack<C>(rdkv, t * rowb + h * d * 2u + lane_prev, z);
+          store_pack<C>(rdsc, t * rowb + h * d * 2u + lane_prev, z);
         }
       }
     }
-    cur = nxt;
+  };
+
+  uint32_t n = wg_in_slice * rows_per_wg + (threadIdx.x >> lgCS);
+  if constexpr (UNI) {
+    // CS >= 64: the lanes of a wave share one row
+    n = __builtin_amdgcn_readfirstlane(n);
+    const UTable<TBL> t{p.seg, tab.cu, tab.off};
+    WinCtxU x;
+    x.S = p.seg.S;
+    x.N = N;
+    x.row_bytes = rowb;
+    x.dout_row_bytes = d * 2u;
+    x.oob_io = p.io_bytes;
+    x.oob_do = N * d * 2u;
+    x.lane_own = lane_own;
+    x.lane_prev = lane_prev;
+    x.lane_gd = g * C * 2u;
+    x.rkv = rkv;
+    x.rsc = rsc;
+    x.rdo = rdo;
+    int s_hint = 0;
+    if (n < N && nstride != 0) {
+      // two windows in flight, alternating roles (no register copies)
+      Window<R, CO, C, true> wa, wb;
+      fetch_window_u(wa, n, s_hint, t, x);
+      for (;;) {
+        fetch_window_u(wb, n + nstride, s_hint, t, x);
+        body(wa);
+        n += nstride;
+        if (n >= N) break;
+        fetch_window_u(wa, n + nstride, s_hint, t, x);
+        body(wb);
+        n += nstride;
+        if (n >= N) break;
+      }
+    }
+  } else {
+    WinCtx x;
+    x.cu = tab.cu;
+    x.off = tab.off;
+    x.S = p.seg.S;
+    x.N = N;
+    x.W = W;
+    x.d = d;
+    x.g = g;
+    x.oob_io = p.io_bytes;
+    x.oob_do = N * d * 2u;
+    x.rkv = rkv;
+    x.rsc = rsc;
+    x.rdo = rdo;
+    Window<R, CO, C, true> cur, nxt;
+    fetch_window(cur, n, x);
+    for (; n < N && nstride != 0; n += nstride) {
+      fetch_window(nxt, n + nstride, x);
+      body(cur);
+      cur = nxt;
+    }
   }
 
   // ---- dAPE: fixed-order reduction inside the workgroup ----
@@ -795,56 +954,76 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     }
     __syncthreads();
   }
-  // 3) one partial row per workgroup of a slice: partial[row][i][h*d + col]
+  // 3) one partial row per workgroup of a slice, stored in column blocks of
+  //    kPartBlock floats: value j = i*W + h*d + col of partial row `row` is at
+  //    ((j / kPartBlock) * rows + row) * kPartBlock + j % kPartBlock, so the
+  //    reduce reads each column block as one contiguous run
   const uint32_t cbase = slice * CW;
-  const rsrc_t rpart = make_rsrc(p.partials, p.partial_rows * R * W * 4u);
+  const uint32_t prow = p.partial_rows;
+  const uint32_t nblk = (R * W + kPartBlock - 1) / kPartBlock;
+  const rsrc_t rpart = make_rsrc(p.partials, nblk * prow * kPartBlock * 4u);
   for (uint32_t idx = threadIdx.x; idx < CO * R * CW; idx += NT) {
     const uint32_t hi = idx / CW, c = idx - hi * CW;
     const uint32_t h = hi / R, i = hi - h * R;
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(red[idx]), rpart,
-                                          ((wg_in_slice * R + i) * W + h * d + cbase + c) * 4u, 0, 0);
+    const uint32_t j = i * W + h * d + cbase + c;
+    const uint32_t o = ((j / kPartBlock) * prow + wg_in_slice) * kPartBlock + (j % kPartBlock);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(red[idx]), rpart, o * 4u, 0, 0);
   }
 }
 
 // ---------------------------------------------------------------------------
 // dAPE reduce: dape[j] = sum over partial rows, in a fixed order.
-// Workgroup = 16 waves x 64 columns; wave w sums rows w, w+16, w+32, ... in
-// increasing order (loads issued 16 at a time so the whole column slice is
-// in flight at once), then the 16 wave totals are added in wave order.
+// A workgroup owns one column block (kPartBlock consecutive columns, stored
+// contiguously for all partial rows).  Thread t takes the 4-column group
+// (t mod 8) and the rows r = t/8, t/8 + 32, ... in increasing order (every
+// load of the thread issued before the first add, so the block is one round
+// trip from memory); the 32 row-group sums of a column are then added in
+// row-group order through LDS.  The order depends only on the problem, not
+// on timing: deterministic.
 // ---------------------------------------------------------------------------
-constexpr int kReduceNT = 1024;
-constexpr int kReduceWaves = kReduceNT / 64;
-constexpr int kReduceBatch = 16;
+constexpr int kReduceNT = 256;
+constexpr int kReduceQuads = kPartBlock / 4;               // 8 float4 per row
+constexpr int kReduceGroups = kReduceNT / kReduceQuads;    // 32 row groups
+constexpr int kReduceBatch = 8;
 
 __global__ __launch_bounds__(kReduceNT) void dape_reduce_kernel(ReduceParams p) {
-  __shared__ float part[kReduceWaves][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t col = blockIdx.x * 64 + lane;
+  __shared__ f32x4 part[kReduceGroups][kReduceQuads];
+  const uint32_t q = threadIdx.x % kReduceQuads, rg = threadIdx.x / kReduceQuads;
   const uint32_t cols = p.cols, rows = p.rows;
+  const uint32_t nblk = (cols + kPartBlock - 1) / kPartBlock;
   // the validity flag is loaded alongside the partials and checked before
   // anything is stored (bad cu_seqlens: dape is left untouched)
   const int32_t flag = __builtin_nontemporal_load(p.ws_flag);
-  const rsrc_t rpart = make_rsrc(p.partials, rows * cols * 4u);
-  float s = 0.0f;
-  if (col < cols) {
-    for (uint32_t base = wave; base < rows; base += kReduceWaves * kReduceBatch) {
-      float v[kReduceBatch];
+  const uint32_t bytes = nblk * rows * kPartBlock * 4u;
+  const rsrc_t rpart = make_rsrc(p.partials, bytes);
+  const uint32_t base_off = (blockIdx.x * rows * kPartBlock + q * 4) * 4u;
+  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (uint32_t base = rg; base < rows; base += kReduceGroups * kReduceBatch) {
+    u32x4 v[kReduceBatch];
 #pragma unroll
-      for (int u = 0; u < kReduceBatch; ++u)
-        v[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            rpart, ((base + u * kReduceWaves) * cols + col) * 4u, 0, 0));
+    for (int u = 0; u < kReduceBatch; ++u) {
+      const uint32_t r = base + u * kReduceGroups;
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rpart, r < rows ? base_off + r * kPartBlock * 4u : bytes, 0, 0);
+    }
 #pragma unroll
-      for (int u = 0; u < kReduceBatch; ++u)
-        if (base + u * kReduceWaves < rows) s = s + v[u];
+    for (int u = 0; u < kReduceBatch; ++u) {
+      if (base + u * kReduceGroups < rows) {
+        s.x = s.x + __uint_as_float(v[u].x);
+        s.y = s.y + __uint_as_float(v[u].y);
+        s.z = s.z + __uint_as_float(v[u].z);
+        s.w = s.w + __uint_as_float(v[u].w);
+      }
     }
   }
-  part[wave][lane] = s;
+  part[rg][q] = s;
   __syncthreads();
-  if (wave == 0 && col < cols && flag == 1) {
-    float t = part[0][lane];
-#pragma unroll
-    for (int w = 1; w < kReduceWaves; ++w) t = t + part[w][lane];
-    p.dape[col] = t;
+  if (threadIdx.x < kPartBlock) {
+    const uint32_t qq = threadIdx.x / 4, k = threadIdx.x % 4;
+    const uint32_t col = blockIdx.x * kPartBlock + threadIdx.x;
+    float t = part[0][qq][k];
+#pragma unroll 8
+    for (int g = 1; g < kReduceGroups; ++g) t = t + part[g][qq][k];
+    if (col < cols && flag == 1) p.dape[col] = t;
   }
 }
 
@@ -888,26 +1067,42 @@ __global__ __launch_bounds__(kScanNT) void seg_scan_kernel(SegParams sp, int32_t
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <int R, int CO, int C>
-static void launch_fwd_rcc(const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
+template <int R, int CO, int C, bool UNI>
+static void launch_fwd_rccu(const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
   const dim3 grid(sh.grid), block(kFwdThreads);
   if (p.seg.table == kTableGlobal)
-    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableGlobal>), grid, block, sh.lds_bytes, st, p);
+    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableGlobal, UNI>), grid, block, sh.lds_bytes, st, p);
   else if (p.seg.table == kTableArgs)
-    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableArgs>), grid, block, sh.lds_bytes, st, p);
+    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableArgs, UNI>), grid, block, sh.lds_bytes, st, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableLds>), grid, block, sh.lds_bytes, st, p);
+    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableLds, UNI>), grid, block, sh.lds_bytes, st, p);
+}
+
+template <int R, int CO, int C>
+static void launch_fwd_rcc(const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
+  if (sh.uniform)
+    launch_fwd_rccu<R, CO, C, true>(p, sh, st);
+  else
+    launch_fwd_rccu<R, CO, C, false>(p, sh, st);
+}
+
+template <int R, int CO, int C, int NT, bool UNI>
+static void launch_bwd_rccnu(const BwdParams& p, const LaunchShape& sh, hipStream_t st) {
+  const dim3 grid(sh.grid), block(NT);
+  if (p.seg.table == kTableGlobal)
+    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableGlobal, UNI>), grid, block, sh.lds_bytes, st, p);
+  else if (p.seg.table == kTableArgs)
+    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableArgs, UNI>), grid, block, sh.lds_bytes, st, p);
+  else
+    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableLds, UNI>), grid, block, sh.lds_bytes, st, p);
 }
 
 template <int R, int CO, int C, int NT>
 static void launch_bwd_rccn(const BwdParams& p, const LaunchShape& sh, hipStream_t st) {
-  const dim3 grid(sh.grid), block(NT);
-  if (p.seg.table == kTableGlobal)
-    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableGlobal>), grid, block, sh.lds_bytes, st, p);
-  else if (p.seg.table == kTableArgs)
-    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableArgs>), grid, block, sh.lds_bytes, st, p);
+  if (sh.uniform)
+    launch_bwd_rccnu<R, CO, C, NT, true>(p, sh, st);
   else
-    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableLds>), grid, block, sh.lds_bytes, st, p);
+    launch_bwd_rccnu<R, CO, C, NT, false>(p, sh, st);
 }
 
 template <int R, int CO>
@@ -924,7 +1119,13 @@ static bool launch_bwd_rcc(const BwdParams& p, const LaunchShape& sh, hipStream_
   switch (sh.threads) {
     case 256: launch_bwd_rccn<R, CO, C, 256>(p, sh, st); return true;
     case 512: launch_bwd_rccn<R, CO, C, 512>(p, sh, st); return true;
-    case 1024: launch_bwd_rccn<R, CO, C, 1024>(p, sh, st); return true;
+    case 1024:
+      // 4 columns per lane at 1024 threads would spill (the planner caps it)
+      if constexpr (C != 4) {
+        launch_bwd_rccn<R, CO, C, 1024>(p, sh, st);
+        return true;
+      }
+      break;
   }
   return false;
 }
@@ -955,7 +1156,7 @@ bool launch_bwd(int ratio, int coff, const BwdParams& p, const LaunchShape& sh, 
 }
 
 void launch_dape_reduce(const ReduceParams& p, hipStream_t st) {
-  const uint32_t grid = (p.cols + 63) / 64;
+  const uint32_t grid = (p.cols + kPartBlock - 1) / kPartBlock;
   hipLaunchKernelGGL(dape_reduce_kernel, dim3(grid), dim3(kReduceNT), 0, st, p);
 }
 

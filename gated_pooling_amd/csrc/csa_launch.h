@@ -16,6 +16,10 @@ constexpr int kMaxLdsSegments = 2048;
 // given take cu and the block offsets as kernel arguments.
 constexpr int kArgSegments = 32;
 
+// dAPE partial rows are stored in column blocks of this many floats (one
+// 128-byte line per partial row and block).
+constexpr int kPartBlock = 32;
+
 // Where the kernels find the segment table.
 enum TableKind : int32_t {
   kTableLds = 0,     // built per workgroup in LDS from the device cu_seqlens
@@ -54,7 +58,7 @@ struct BwdParams {
   const uint16_t* dout;
   uint16_t* dkv;
   uint16_t* dscore;
-  float* partials;        // [partial_rows, ratio, coff * head_dim] in the workspace
+  float* partials;        // column blocks [ceil(ratio*W/kPartBlock)][partial_rows][kPartBlock]
   int32_t* ws_flag;       // validity flag in the workspace
   uint32_t io_bytes;
   uint32_t head_dim;
@@ -77,6 +81,7 @@ struct LaunchShape {
   uint32_t grid;
   uint32_t threads;
   uint32_t cols;          // output columns per lane (2, 4 or 8)
+  bool uniform;           // every wave works on one output row at a time
   size_t lds_bytes;
 };
 

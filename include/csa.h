@@ -85,8 +85,8 @@ typedef enum csa_status {
     CSA_STATUS_INVALID_VALUE = 1,
     /* outside the validated envelope: ratio not in {2, 4}, coff not in
      * {1, 2}, head_dim not a power of two in [2, 1024], or one of
-     * total_tokens*coff*head_dim, total_comp*head_dim, ratio*coff*head_dim
-     * not below 2^31 (each checked on its own) */
+     * (total_tokens+1)*coff*head_dim, total_comp*head_dim,
+     * ratio*coff*head_dim not below 2^31 (each checked on its own) */
     CSA_STATUS_NOT_SUPPORTED = 2,
     /* workspace_bytes below the size the *_workspace_size query returns */
     CSA_STATUS_WORKSPACE_TOO_SMALL = 3,

@@ -75,6 +75,7 @@ def test_workloads_are_supported(name):
     ((4, 2, 96, 2, 64, 15), G.CsaNotSupported),       # not a power of two
     ((4, 2, 2048, 2, 64, 15), G.CsaNotSupported),     # beyond the launch bound
     ((4, 2, 512, 1, 2 ** 21, 1), G.CsaNotSupported),  # total_tokens*W = 2^31
+    ((4, 2, 512, 1, 2 ** 21 - 1, 1), G.CsaNotSupported),  # (total_tokens+1)*W = 2^31
     ((4, 1, 16, 1, 100, 26), G.CsaInvalidValue),      # N*ratio > T
     ((4, 2, 16, 1, 3, 1), G.CsaInvalidValue),         # total_comp > 0, total_tokens < ratio
     ((2, 2, 16, 1, 1, 1), G.CsaInvalidValue),         # same at ratio 2
@@ -94,7 +95,7 @@ def test_check_support_size_limits_are_independent():
     with pytest.raises(G.CsaNotSupported):
         G.csa_compressor_check_support(2, 1, 1024, 1, 2 ** 22, 2 ** 21)
     # just below every limit is accepted
-    G.csa_compressor_check_support(4, 2, 512, 1, 2 ** 21 - 1, 2 ** 18)
+    G.csa_compressor_check_support(4, 2, 512, 1, 2 ** 21 - 2, 2 ** 18)
     G.csa_compressor_check_support(2, 2, 2, 1, 4, 2)
     G.csa_compressor_check_support(4, 1, 1024, 3, 0, 0)
 
