@@ -23,6 +23,9 @@
 //   CSA_BWD_MAX_WGS   backward grid cap (main workgroups)
 //   CSA_BWD_SLICE_BYTES  bytes of a half-row one backward workgroup covers
 //                     (>= 128; smaller slices shrink the dAPE partials)
+//   CSA_UNIFORM       1: wave-uniform row path where a row has >= 64 chunks
+//   CSA_FWD_PREFETCH, CSA_BWD_PREFETCH  windows in flight per lane on the
+//                     uniform path (2, 3, 4)
 
 #include <stdarg.h>
 #include <stdio.h>
@@ -61,6 +64,8 @@ struct Tuning {
   int bwd_max_wgs = 256;
   int bwd_slice_bytes = 512;
   int uniform = 1;        // wave-uniform row path where a row has >= 64 chunks
+  int fwd_prefetch = 2;   // windows in flight per lane (uniform path)
+  int bwd_prefetch = 3;
 };
 
 int env_int(const char* name, int dflt, const int* allowed, int n_allowed, int lo, int hi) {
@@ -89,6 +94,8 @@ const Tuning& tuning() {
     d.bwd_max_wgs = env_int("CSA_BWD_MAX_WGS", d.bwd_max_wgs, nullptr, 0, 1, 1 << 16);
     d.bwd_slice_bytes = env_int("CSA_BWD_SLICE_BYTES", d.bwd_slice_bytes, nullptr, 0, 16, 1 << 16);
     d.uniform = env_int("CSA_UNIFORM", d.uniform, nullptr, 0, 0, 1);
+    d.fwd_prefetch = env_int("CSA_FWD_PREFETCH", d.fwd_prefetch, nullptr, 0, 2, 4);
+    d.bwd_prefetch = env_int("CSA_BWD_PREFETCH", d.bwd_prefetch, nullptr, 0, 2, 4);
     return d;
   }();
   return t;
@@ -179,6 +186,7 @@ Plan make_plan(const Problem& p) {
     pl.fwd.threads = csa::kFwdThreads;
     pl.fwd.cols = C;
     pl.fwd.uniform = tu.uniform && G >= 64;
+    pl.fwd.prefetch = pl.fwd.uniform ? tu.fwd_prefetch : 2;
     pl.fwd_log2_chunks = log2i(G);
     const uint64_t table_words = pl.global_table ? 0 : 2 * (csa::kFwdThreads / 64) + 2 * uint64_t(p.S + 1);
     pl.fwd.lds_bytes = table_words * 4;
@@ -216,6 +224,7 @@ Plan make_plan(const Problem& p) {
     pl.bwd.threads = NT;
     pl.bwd.cols = C;
     pl.bwd.uniform = tu.uniform && CS >= 64;
+    pl.bwd.prefetch = (pl.bwd.uniform && NT <= 512) ? tu.bwd_prefetch : 2;
     pl.bwd_log2_chunks = log2i(G);
     pl.bwd_log2_slice = log2i(CS);
     pl.bwd_main_wgs = static_cast<uint32_t>(main);

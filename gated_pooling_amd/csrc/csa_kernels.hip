@@ -519,6 +519,25 @@ __device__ __forceinline__ void fetch_window_u(Window<R, CO, C, BWD>& w, uint32_
   if constexpr (BWD) w.gd[0] = load_pack<C>(x.rdo, x.lane_gd + (valid ? n * x.dout_row_bytes : x.oob_do));
 }
 
+// PF windows in flight along a lane's walk n, n + ns, n + 2 ns, ... < N:
+// window k of the ring is computed while the next PF - 1 are loading.  The
+// ring is unrolled, so each window keeps its own registers (no copies).
+template <int PF, typename Win, typename Fetch, typename Body>
+__device__ __forceinline__ void window_ring(uint32_t n, uint32_t ns, uint32_t N, Fetch&& fetch, Body&& body) {
+  Win w[PF];
+#pragma unroll
+  for (int k = 0; k < PF - 1; ++k) fetch(w[k], n + k * ns);
+  for (;;) {
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+      fetch(w[(k + PF - 1) % PF], n + (PF - 1) * ns);
+      body(w[k], n);
+      n += ns;
+      if (n >= N) return;
+    }
+  }
+}
+
 // Forward of one window: the C output columns packed as bf16.
 template <int R, int CO, int C, bool BWD>
 __device__ __forceinline__ Pack<C> fwd_window(const Window<R, CO, C, BWD>& w, const float (&ape_r)[CO][R][C]) {
@@ -565,7 +584,7 @@ __device__ __forceinline__ Pack<C> fwd_window(const Window<R, CO, C, BWD>& w, co
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
-template <int R, int CO, int C, int NT, int TBL, bool UNI>
+template <int R, int CO, int C, int NT, int TBL, bool UNI, int PF>
 __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
   extern __shared__ int32_t lds[];
   SegTable tab{nullptr, nullptr};
@@ -613,19 +632,10 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
     x.rdo = rkv;
     const uint32_t lane_out = g * C * 2u, out_row = d * 2u;
     int s_hint = 0;
-    // two windows in flight, alternating roles (no register copies)
-    Window<R, CO, C, false> wa, wb;
-    fetch_window_u(wa, n, s_hint, t, x);
-    for (;;) {
-      fetch_window_u(wb, n + nstride, s_hint, t, x);
-      store_pack<C>(rout, n * out_row + lane_out, fwd_window(wa, ape_r));
-      n += nstride;
-      if (n >= N) break;
-      fetch_window_u(wa, n + nstride, s_hint, t, x);
-      store_pack<C>(rout, n * out_row + lane_out, fwd_window(wb, ape_r));
-      n += nstride;
-      if (n >= N) break;
-    }
+    using Win = Window<R, CO, C, false>;
+    window_ring<PF, Win>(
+        n, nstride, N, [&](Win& w, uint32_t m) { fetch_window_u(w, m, s_hint, t, x); },
+        [&](const Win& w, uint32_t m) { store_pack<C>(rout, m * out_row + lane_out, fwd_window(w, ape_r)); });
   } else {
     WinCtx x;
     x.cu = tab.cu;
@@ -690,7 +700,7 @@ __device__ void zero_sweep(const BwdParams& p, const SegTable& tab) {
   zero_range(rdsc, b0, b1, zid * NT + threadIdx.x, nz * NT);
 }
 
-template <int R, int CO, int C, int NT, int TBL, bool UNI>
+template <int R, int CO, int C, int NT, int TBL, bool UNI, int PF>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   extern __shared__ int32_t lds[];
   SegTable tab{nullptr, nullptr};
@@ -886,19 +896,10 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     x.rdo = rdo;
     int s_hint = 0;
     if (n < N && nstride != 0) {
-      // two windows in flight, alternating roles (no register copies)
-      Window<R, CO, C, true> wa, wb;
-      fetch_window_u(wa, n, s_hint, t, x);
-      for (;;) {
-        fetch_window_u(wb, n + nstride, s_hint, t, x);
-        body(wa);
-        n += nstride;
-        if (n >= N) break;
-        fetch_window_u(wa, n + nstride, s_hint, t, x);
-        body(wb);
-        n += nstride;
-        if (n >= N) break;
-      }
+      using Win = Window<R, CO, C, true>;
+      window_ring<PF, Win>(
+          n, nstride, N, [&](Win& w, uint32_t m) { fetch_window_u(w, m, s_hint, t, x); },
+          [&](const Win& w, uint32_t) { body(w); });
     }
   } else {
     WinCtx x;
@@ -1067,49 +1068,68 @@ __global__ __launch_bounds__(kScanNT) void seg_scan_kernel(SegParams sp, int32_t
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <int R, int CO, int C, bool UNI>
+template <int R, int CO, int C, bool UNI, int PF>
 static void launch_fwd_rccu(const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
   const dim3 grid(sh.grid), block(kFwdThreads);
   if (p.seg.table == kTableGlobal)
-    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableGlobal, UNI>), grid, block, sh.lds_bytes, st, p);
+    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableGlobal, UNI, PF>), grid, block, sh.lds_bytes, st, p);
   else if (p.seg.table == kTableArgs)
-    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableArgs, UNI>), grid, block, sh.lds_bytes, st, p);
+    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableArgs, UNI, PF>), grid, block, sh.lds_bytes, st, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableLds, UNI>), grid, block, sh.lds_bytes, st, p);
+    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableLds, UNI, PF>), grid, block, sh.lds_bytes, st, p);
 }
 
 template <int R, int CO, int C>
-static void launch_fwd_rcc(const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
-  if (sh.uniform)
-    launch_fwd_rccu<R, CO, C, true>(p, sh, st);
-  else
-    launch_fwd_rccu<R, CO, C, false>(p, sh, st);
+static bool launch_fwd_rcc(const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
+  if (!sh.uniform) {
+    launch_fwd_rccu<R, CO, C, false, 2>(p, sh, st);
+    return true;
+  }
+  switch (sh.prefetch) {
+    case 2: launch_fwd_rccu<R, CO, C, true, 2>(p, sh, st); return true;
+    case 3: launch_fwd_rccu<R, CO, C, true, 3>(p, sh, st); return true;
+    case 4: launch_fwd_rccu<R, CO, C, true, 4>(p, sh, st); return true;
+  }
+  return false;
 }
 
-template <int R, int CO, int C, int NT, bool UNI>
+template <int R, int CO, int C, int NT, bool UNI, int PF>
 static void launch_bwd_rccnu(const BwdParams& p, const LaunchShape& sh, hipStream_t st) {
   const dim3 grid(sh.grid), block(NT);
   if (p.seg.table == kTableGlobal)
-    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableGlobal, UNI>), grid, block, sh.lds_bytes, st, p);
+    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableGlobal, UNI, PF>), grid, block, sh.lds_bytes, st, p);
   else if (p.seg.table == kTableArgs)
-    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableArgs, UNI>), grid, block, sh.lds_bytes, st, p);
+    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableArgs, UNI, PF>), grid, block, sh.lds_bytes, st, p);
   else
-    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableLds, UNI>), grid, block, sh.lds_bytes, st, p);
+    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableLds, UNI, PF>), grid, block, sh.lds_bytes, st, p);
 }
 
 template <int R, int CO, int C, int NT>
-static void launch_bwd_rccn(const BwdParams& p, const LaunchShape& sh, hipStream_t st) {
-  if (sh.uniform)
-    launch_bwd_rccnu<R, CO, C, NT, true>(p, sh, st);
-  else
-    launch_bwd_rccnu<R, CO, C, NT, false>(p, sh, st);
+static bool launch_bwd_rccn(const BwdParams& p, const LaunchShape& sh, hipStream_t st) {
+  if (!sh.uniform) {
+    launch_bwd_rccnu<R, CO, C, NT, false, 2>(p, sh, st);
+    return true;
+  }
+  if constexpr (NT <= 512) {
+    switch (sh.prefetch) {
+      case 2: launch_bwd_rccnu<R, CO, C, NT, true, 2>(p, sh, st); return true;
+      case 3: launch_bwd_rccnu<R, CO, C, NT, true, 3>(p, sh, st); return true;
+      case 4: launch_bwd_rccnu<R, CO, C, NT, true, 4>(p, sh, st); return true;
+    }
+    return false;
+  } else {
+    // 1024-thread workgroups: deeper rings would not fit the registers
+    if (sh.prefetch != 2) return false;
+    launch_bwd_rccnu<R, CO, C, NT, true, 2>(p, sh, st);
+    return true;
+  }
 }
 
 template <int R, int CO>
 static bool launch_fwd_rc(const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
   switch (sh.cols) {
-    case 4: launch_fwd_rcc<R, CO, 4>(p, sh, st); return true;
-    case 2: launch_fwd_rcc<R, CO, 2>(p, sh, st); return true;
+    case 4: return launch_fwd_rcc<R, CO, 4>(p, sh, st);
+    case 2: return launch_fwd_rcc<R, CO, 2>(p, sh, st);
   }
   return false;
 }
@@ -1117,14 +1137,11 @@ static bool launch_fwd_rc(const FwdParams& p, const LaunchShape& sh, hipStream_t
 template <int R, int CO, int C>
 static bool launch_bwd_rcc(const BwdParams& p, const LaunchShape& sh, hipStream_t st) {
   switch (sh.threads) {
-    case 256: launch_bwd_rccn<R, CO, C, 256>(p, sh, st); return true;
-    case 512: launch_bwd_rccn<R, CO, C, 512>(p, sh, st); return true;
+    case 256: return launch_bwd_rccn<R, CO, C, 256>(p, sh, st);
+    case 512: return launch_bwd_rccn<R, CO, C, 512>(p, sh, st);
     case 1024:
       // 4 columns per lane at 1024 threads would spill (the planner caps it)
-      if constexpr (C != 4) {
-        launch_bwd_rccn<R, CO, C, 1024>(p, sh, st);
-        return true;
-      }
+      if constexpr (C != 4) return launch_bwd_rccn<R, CO, C, 1024>(p, sh, st);
       break;
   }
   return false;

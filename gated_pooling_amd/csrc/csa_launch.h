@@ -82,6 +82,7 @@ struct LaunchShape {
   uint32_t threads;
   uint32_t cols;          // output columns per lane (2, 4 or 8)
   bool uniform;           // every wave works on one output row at a time
+  uint32_t prefetch;      // windows in flight per lane (uniform path: 2, 3, 4)
   size_t lds_bytes;
 };
 
