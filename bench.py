@@ -178,8 +178,10 @@ def cpu_baseline(wl, N, kv, sc, ape, dout, budget_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    # the clocks ramp up over the first few milliseconds of load: warm up
+    # long enough that the timed steps see steady state
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--sets", type=int, default=5, help="rotating buffer sets (cold cache)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
