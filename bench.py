@@ -149,6 +149,77 @@ def summarize_counters(fetch_dir, write_dir, workload):
     print(json.dumps(rec["kernels"][workload]))
 
 
+class EagerCompressor:
+    """The same operation written as plain PyTorch fp32 ops (gather the
+    windows, mask the first block's previous half, softmax over the window,
+    weighted sum; backward by autograd).  Timing context only: the pages
+    compare their kernels with an fp32 eager region of this kind
+    [PR710: Performance at ratio=2].  It is not part of libcsa and nothing in
+    the library calls it.
+
+    Index tensors for the windows are built once per pack (host side)."""
+
+    def __init__(self, cu, T, r, c, d, device):
+        import torch
+        prev_rows, own_rows, masked = [], [], []
+        for s in range(len(cu) - 1):
+            for b in range((cu[s + 1] - cu[s]) // r):
+                own = cu[s] + b * r
+                own_rows.append([own + i for i in range(r)])
+                prev_rows.append([own - r + i if b > 0 else own + i for i in range(r)])
+                masked.append(b == 0)
+        self.r, self.c, self.d = r, c, d
+        self.N = len(own_rows)
+        self.own = torch.tensor(own_rows, dtype=torch.long, device=device).reshape(-1, r)
+        self.prev = torch.tensor(prev_rows, dtype=torch.long, device=device).reshape(-1, r)
+        self.masked = torch.tensor(masked, dtype=torch.bool, device=device)
+
+    def forward(self, kv, score, ape):
+        """fp32 leaves kv [T, W], score [T, W], ape [r, W] -> out fp32 [N, d]."""
+        import torch
+        r, c, d = self.r, self.c, self.d
+        if c == 2:
+            x = torch.cat([score[self.prev][:, :, :d] + ape[:, :d], score[self.own][:, :, d:] + ape[:, d:]], dim=1)
+            v = torch.cat([kv[self.prev][:, :, :d], kv[self.own][:, :, d:]], dim=1)
+            mask = torch.zeros(self.N, 2 * r, 1, dtype=torch.bool, device=x.device)
+            mask[:, :r] = self.masked.view(-1, 1, 1)
+            x = x.masked_fill(mask, float("-inf"))
+        else:
+            x = score[self.own] + ape
+            v = kv[self.own]
+        p = torch.softmax(x, dim=1)
+        return (p * v).sum(dim=1)
+
+    def step(self, kv16, score16, ape, dout16):
+        """One fp32 eager forward + backward from the bf16 inputs: returns
+        (out, dkv, dscore, dape) in fp32."""
+        kv = kv16.float().requires_grad_(True)
+        score = score16.float().requires_grad_(True)
+        ape = ape.detach().clone().requires_grad_(True)
+        out = self.forward(kv, score, ape)
+        out.backward(dout16.float())
+        return out.detach(), kv.grad, score.grad, ape.grad
+
+
+def eager_timing(wl, N, sets, stream, steps):
+    """Mean µs per fp32 eager forward + backward step on the GPU, over the
+    same rotating buffer sets as the library."""
+    import torch
+    ec = EagerCompressor(list(wl.cu_seqlens), wl.total_tokens, wl.ratio, wl.coff, wl.head_dim, sets[0]["kv"].device)
+    assert ec.N == N
+    for j in range(len(sets)):
+        ec.step(sets[j]["kv"], sets[j]["sc"], sets[j]["ape"], sets[j]["dout"])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for k in range(steps):
+        st = sets[k % len(sets)]
+        ec.step(st["kv"], st["sc"], st["ape"], st["dout"])
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / steps
+
+
 def cpu_baseline(wl, N, kv, sc, ape, dout, budget_s):
     """Time the CPU oracle (fp32 evaluation order, OpenMP over windows) on the
     same pack: forward + backward, repeated until about budget_s seconds."""
@@ -187,6 +258,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-warm", action="store_true")
+    ap.add_argument("--no-eager", action="store_true", help="skip the fp32 PyTorch eager comparison")
+    ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph replay timing")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/hbm_counters.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
@@ -233,24 +306,25 @@ def main():
         sets.append(st)
     stream = torch.cuda.current_stream()
     sptr = ctypes.c_void_p(stream.cuda_stream)
+    cur = {"s": sptr}  # launch stream (switched to the capture stream while a graph is captured)
     L = G.lib()
     cu_host = G.host_cu(cu)  # host copy: small packs get the segment table as kernel arguments
 
     def fwd(st):
         p = st["p"]
         rc = L.csa_compressor_fwd(p["kv"], p["sc"], p["ape"], p["cu"], cu_host, S, T, N, r, c, d, p["out"],
-                                  p["fws"], st["fws"].numel(), sptr)
+                                  p["fws"], st["fws"].numel(), cur["s"])
         assert rc == 0, G.csa_last_error()
 
     def grads(st):
         p = st["p"]
         rc = L.csa_compressor_bwd_grads(p["kv"], p["sc"], p["ape"], p["cu"], cu_host, S, T, N, r, c, d, p["dout"],
-                                        p["dkv"], p["dsc"], p["bws"], st["bws"].numel(), sptr)
+                                        p["dkv"], p["dsc"], p["bws"], st["bws"].numel(), cur["s"])
         assert rc == 0, G.csa_last_error()
 
     def reduce(st):
         p = st["p"]
-        rc = L.csa_compressor_bwd_dape_reduce(r, c, d, S, T, N, p["dape"], p["bws"], st["bws"].numel(), sptr)
+        rc = L.csa_compressor_bwd_dape_reduce(r, c, d, S, T, N, p["dape"], p["bws"], st["bws"].numel(), cur["s"])
         assert rc == 0, G.csa_last_error()
 
     nsets = len(sets)
@@ -347,6 +421,50 @@ def main():
     copy_gbs = 2 * src.numel() * 2 * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
     del src, dst
 
+    graph = None
+    if not args.no_graph:
+        # the same launches captured once into hipGraphs and replayed: a
+        # forward-only graph and a forward + backward graph over the buffer sets
+        def captured(fn):
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                cur["s"] = ctypes.c_void_p(side.cuda_stream)
+                fn()  # warm-up on the side stream, as torch's capture pattern asks
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                cur["s"] = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+                fn()
+            cur["s"] = sptr
+            torch.cuda.synchronize()
+            return g
+
+        def replay_us(g, reps):
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / (reps * nsets)
+
+        g_fwd = captured(lambda: [fwd(st) for st in sets])
+        g_step = captured(lambda: run_steps(nsets))
+        reps = max(1, K // nsets)
+        graph = {"fwd_us": round(replay_us(g_fwd, reps), 3), "fwd_bwd_us": round(replay_us(g_step, reps), 3)}
+        del g_fwd, g_step
+
+    eager = None
+    if not args.no_eager:
+        eager_us = eager_timing(wl, N, sets, stream, steps=20)
+        eager = {"fwd_bwd_us": round(eager_us, 1), "speedup": round(eager_us / (ms_per_step * 1e3), 1),
+                 "what": "PyTorch fp32 eager forward + autograd backward of the same op, same buffers"}
+
     cpu = None
     if not args.no_cpu_baseline:
         reps, el, cores = cpu_baseline(wl, N, kv, sc, ape, dout, args.cpu_seconds)
@@ -380,6 +498,8 @@ def main():
         "kernels": kern,
         "warm_us": warm,
         "copy_kernel_GBs": round(copy_gbs, 1),
+        "graph_us": graph,
+        "eager": eager,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
         "cpu_baseline": cpu,

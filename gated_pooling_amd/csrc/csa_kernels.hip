@@ -75,12 +75,17 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Cache policy bits of buffer instructions: kAuxStream marks data that is
-// touched once (kv/score reads, dkv/dscore writes) as non-temporal.  Build
-// knob CSA_STREAM_HINT (0 disables the hint).
+// touched once (kv/score/dout reads) as non-temporal, kAuxStreamStore the
+// same for out/dkv/dscore writes.  Build knobs CSA_STREAM_HINT and
+// CSA_STORE_HINT (0 disables a hint).
 #ifndef CSA_STREAM_HINT
 #define CSA_STREAM_HINT 2
 #endif
+#ifndef CSA_STORE_HINT
+#define CSA_STORE_HINT CSA_STREAM_HINT
+#endif
 constexpr int kAuxStream = CSA_STREAM_HINT;
+constexpr int kAuxStreamStore = CSA_STORE_HINT;
 
 template <int C, int AUX = kAuxStream>
 __device__ __forceinline__ Pack<C> load_pack(rsrc_t r, uint32_t byte_off) {
@@ -98,7 +103,7 @@ __device__ __forceinline__ Pack<C> load_pack(rsrc_t r, uint32_t byte_off) {
   return p;
 }
 
-template <int C, int AUX = kAuxStream>
+template <int C, int AUX = kAuxStreamStore>
 __device__ __forceinline__ void store_pack(rsrc_t r, uint32_t byte_off, const Pack<C>& p) {
   if constexpr (C == 8) {
     u32x4 v = {p.w[0], p.w[1], p.w[2], p.w[3]};
