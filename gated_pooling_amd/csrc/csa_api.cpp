@@ -11,8 +11,11 @@
 // total_tokens*coff*head_dim, total_comp*head_dim and ratio*coff*head_dim
 // below 2^31 each, and the rejection of total_comp > 0 with
 // total_tokens < ratio ([PR5984: review-feedback commit; PR710: What]).
-// head_dim must be a power of two in [2, 1024] in this build (the lane
-// layout splits a half-row into power-of-two chunks).
+// head_dim may be any value in [1, 1024]: an odd head_dim takes one column
+// per lane (16-bit accesses), and a row whose chunk count is not a power of
+// two is padded to the next power of two in lanes (the extra lanes are
+// masked) [PR5984: vectorize-forward commit (scalar instantiation for odd
+// head_dims)].
 //
 // Tuning knobs (environment, read once per process; every value is
 // validated and falls back to the default):
@@ -119,8 +122,8 @@ csa_status_t check_problem(const Problem& p) {
     return fail(CSA_STATUS_NOT_SUPPORTED, "ratio must be 2 or 4 (got %d)", p.ratio);
   if (p.coff != 1 && p.coff != 2)
     return fail(CSA_STATUS_NOT_SUPPORTED, "coff must be 1 or 2 (got %d)", p.coff);
-  if (!is_pow2(p.head_dim) || p.head_dim < 2 || p.head_dim > 1024)
-    return fail(CSA_STATUS_NOT_SUPPORTED, "head_dim must be a power of two in [2, 1024] (got %d)", p.head_dim);
+  if (p.head_dim < 1 || p.head_dim > 1024)
+    return fail(CSA_STATUS_NOT_SUPPORTED, "head_dim must be in [1, 1024] (got %d)", p.head_dim);
   if (p.S < 0 || p.T < 0 || p.N < 0)
     return fail(CSA_STATUS_INVALID_VALUE, "negative size: num_segments=%d total_tokens=%lld total_comp=%lld",
                 p.S, (long long)p.T, (long long)p.N);
@@ -153,10 +156,12 @@ struct Plan {
   // forward
   csa::LaunchShape fwd;
   int fwd_log2_chunks;
+  uint32_t fwd_chunks;
   uint64_t ws_fwd;
   // backward
   csa::LaunchShape bwd;
   int bwd_log2_chunks;
+  uint32_t bwd_chunks;
   int bwd_log2_slice;
   uint32_t bwd_main_wgs;
   uint32_t partial_rows;
@@ -167,6 +172,19 @@ struct Plan {
 
 constexpr uint64_t kHeaderBytes = 256;
 
+// Columns per lane: 1 for an odd head_dim; otherwise the requested 2 or 4
+// when it divides head_dim into a power-of-two number of chunks, else 2.
+int choose_cols(int head_dim, int want) {
+  if (head_dim & 1) return 1;
+  if (want == 4 && (head_dim % 4 != 0 || !is_pow2(head_dim / 4))) return 2;
+  return want;
+}
+int64_t pow2_ceil(int64_t x) {
+  int64_t p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
 Plan make_plan(const Problem& p) {
   const Tuning& tu = tuning();
   Plan pl{};
@@ -176,36 +194,42 @@ Plan make_plan(const Problem& p) {
 
   // forward: one lane per (output row, chunk of C columns), grid-stride
   {
-    const int C = p.head_dim < tu.fwd_cols ? p.head_dim : tu.fwd_cols;
-    const int64_t G = p.head_dim / C;
-    const int64_t lanes = p.N * G;
+    const int C = choose_cols(p.head_dim, tu.fwd_cols);
+    const int64_t G = p.head_dim / C;     // chunks of a row
+    const int64_t Gp = pow2_ceil(G);      // lanes of a row
+    const int64_t lanes = p.N * Gp;
     int64_t wgs = (lanes + csa::kFwdThreads - 1) / csa::kFwdThreads;
     if (wgs > tu.fwd_max_wgs) wgs = tu.fwd_max_wgs;
-    if (G > csa::kFwdThreads) wgs = align_up(wgs, G / csa::kFwdThreads);  // lanes % G == 0
+    if (Gp > csa::kFwdThreads) wgs = align_up(wgs, Gp / csa::kFwdThreads);  // lanes % Gp == 0
     pl.fwd.grid = static_cast<uint32_t>(wgs);
     pl.fwd.threads = csa::kFwdThreads;
     pl.fwd.cols = C;
-    pl.fwd.uniform = tu.uniform && G >= 64;
-    pl.fwd.prefetch = pl.fwd.uniform ? tu.fwd_prefetch : 2;
-    pl.fwd_log2_chunks = log2i(G);
+    pl.fwd.pad = Gp != G || C == 1;
+    pl.fwd.uniform = tu.uniform && Gp >= 64;
+    pl.fwd.prefetch = (pl.fwd.uniform && !pl.fwd.pad) ? tu.fwd_prefetch : 2;
+    pl.fwd_log2_chunks = log2i(Gp);
+    pl.fwd_chunks = static_cast<uint32_t>(G);
     const uint64_t table_words = pl.global_table ? 0 : 2 * (csa::kFwdThreads / 64) + 2 * uint64_t(p.S + 1);
     pl.fwd.lds_bytes = table_words * 4;
     pl.ws_fwd = pl.global_table ? kHeaderBytes + pl.off_bytes : 0;
   }
   // backward
   {
-    const int C = p.head_dim < tu.bwd_cols ? p.head_dim : tu.bwd_cols;
-    // 4 columns per lane need more than 128 VGPRs: at most 512 threads
-    const int NT = (C == 4 && tu.bwd_threads > 512) ? 512 : tu.bwd_threads;
-    const int64_t G = p.head_dim / C;
+    const int C = choose_cols(p.head_dim, tu.bwd_cols);
+    const int64_t G = p.head_dim / C;     // chunks of a row
+    const int64_t Gp = pow2_ceil(G);      // lanes of a row
+    const bool pad = Gp != G || C == 1;
+    // 4 columns per lane need more than 128 VGPRs: at most 512 threads;
+    // padded rows use 256-thread workgroups
+    const int NT = pad ? 256 : (C == 4 && tu.bwd_threads > 512) ? 512 : tu.bwd_threads;
     // column slice per workgroup: at least 128 bytes of a half-row per wave
     // row (whole cache lines), at most the whole row and the workgroup
     int64_t CS = tu.bwd_slice_bytes / (2 * C);
     if (CS < 64 / C) CS = 64 / C;
-    if (CS > G) CS = G;
+    if (CS > Gp) CS = Gp;
     if (CS > NT) CS = NT;
-    const int64_t slices = G / CS;
-    const int64_t lanes = p.N * G;
+    const int64_t slices = Gp / CS;
+    const int64_t lanes = p.N * Gp;
     int64_t main = (lanes + NT - 1) / NT;
     if (main > tu.bwd_max_wgs) main = tu.bwd_max_wgs;
     main = align_up(main, slices);  // whole slices
@@ -223,9 +247,11 @@ Plan make_plan(const Problem& p) {
     pl.bwd.grid = static_cast<uint32_t>(main + zero);
     pl.bwd.threads = NT;
     pl.bwd.cols = C;
+    pl.bwd.pad = pad;
     pl.bwd.uniform = tu.uniform && CS >= 64;
-    pl.bwd.prefetch = (pl.bwd.uniform && NT <= 512) ? tu.bwd_prefetch : 2;
-    pl.bwd_log2_chunks = log2i(G);
+    pl.bwd.prefetch = (pl.bwd.uniform && NT <= 512 && !pad) ? tu.bwd_prefetch : 2;
+    pl.bwd_log2_chunks = log2i(Gp);
+    pl.bwd_chunks = static_cast<uint32_t>(G);
     pl.bwd_log2_slice = log2i(CS);
     pl.bwd_main_wgs = static_cast<uint32_t>(main);
     pl.partial_rows = static_cast<uint32_t>(main / slices);
@@ -346,6 +372,7 @@ csa_status_t launch_bwd_grads(const Problem& pr, const Plan& pl, const void* kv,
   bp.io_bytes = static_cast<uint32_t>(pr.T * pr.coff * pr.head_dim * 2);
   bp.head_dim = pr.head_dim;
   bp.log2_chunks = pl.bwd_log2_chunks;
+  bp.chunks = pl.bwd_chunks;
   bp.log2_slice = pl.bwd_log2_slice;
   bp.main_wgs = pl.bwd_main_wgs;
   bp.partial_rows = pl.partial_rows;
@@ -455,6 +482,7 @@ csa_status_t csa_compressor_fwd(const void* kv, const void* score, const float* 
   fp.io_bytes = static_cast<uint32_t>(pr.T * pr.coff * pr.head_dim * 2);
   fp.head_dim = head_dim;
   fp.log2_chunks = pl.fwd_log2_chunks;
+  fp.chunks = pl.fwd_chunks;
   if (!csa::launch_fwd(ratio, coff, fp, pl.fwd, stream))
     return fail(CSA_STATUS_NOT_SUPPORTED, "no forward kernel for this configuration");
   return after_launch("forward");

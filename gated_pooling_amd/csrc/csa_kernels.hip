@@ -62,12 +62,17 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 }
 
 // ---------------------------------------------------------------------------
-// C bf16 values of one row chunk, as C/2 packed dwords.
+// C bf16 values of one row chunk, as C/2 packed dwords (C = 1: the value in
+// the low half of one dword).
 // ---------------------------------------------------------------------------
 template <int C>
 struct Pack {
-  uint32_t w[C / 2];
+  uint32_t w[(C + 1) / 2];
 };
+
+// Columns of a chunk processed together by the softmax (2, or 1 at C = 1).
+template <int C>
+constexpr int kColGroup = C >= 2 ? 2 : 1;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -96,9 +101,11 @@ __device__ __forceinline__ Pack<C> load_pack(rsrc_t r, uint32_t byte_off) {
   } else if constexpr (C == 4) {
     u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, AUX);
     p.w[0] = v.x; p.w[1] = v.y;
-  } else {
-    static_assert(C == 2, "C must be 2, 4 or 8");
+  } else if constexpr (C == 2) {
     p.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, AUX);
+  } else {
+    static_assert(C == 1, "C must be 1, 2, 4 or 8");
+    p.w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, AUX);
   }
   return p;
 }
@@ -111,8 +118,10 @@ __device__ __forceinline__ void store_pack(rsrc_t r, uint32_t byte_off, const Pa
   } else if constexpr (C == 4) {
     u32x2 v = {p.w[0], p.w[1]};
     __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, AUX);
-  } else {
+  } else if constexpr (C == 2) {
     __builtin_amdgcn_raw_buffer_store_b32(p.w[0], r, byte_off, 0, AUX);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(p.w[0]), r, byte_off, 0, AUX);
   }
 }
 
@@ -130,9 +139,11 @@ __device__ __forceinline__ void load_f32(rsrc_t r, uint32_t byte_off, float (&ou
     u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
     out[0] = __uint_as_float(a.x); out[1] = __uint_as_float(a.y);
     out[2] = __uint_as_float(a.z); out[3] = __uint_as_float(a.w);
-  } else {
+  } else if constexpr (C == 2) {
     u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
     out[0] = __uint_as_float(a.x); out[1] = __uint_as_float(a.y);
+  } else {
+    out[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
   }
 }
 
@@ -150,6 +161,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   v.x = static_cast<__bf16>(lo);
   v.y = static_cast<__bf16>(hi);
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// One column group's results packed as bf16: two columns, or one column in
+// the low half (C = 1).
+template <int NG>
+__device__ __forceinline__ uint32_t pack_group(const float (&o)[NG]) {
+  if constexpr (NG == 2) return pack_bf16x2(o[0], o[1]);
+  else return pack_bf16x2(o[0], 0.0f);
+}
+template <int NG, int K>
+__device__ __forceinline__ uint32_t pack_group_at(const float (&a)[NG][K], int i) {
+  if constexpr (NG == 2) return pack_bf16x2(a[0][i], a[1][i]);
+  else return pack_bf16x2(a[0][i], 0.0f);
 }
 
 // ---------------------------------------------------------------------------
@@ -417,6 +441,7 @@ struct WinCtx {
   uint32_t N, W, d, g;
   uint32_t oob_io, oob_do;                 // past-the-end offsets (masked loads)
   rsrc_t rkv, rsc, rdo;
+  bool active;                             // the lane's chunk is inside the row
 };
 
 template <int R, int CO, int C, bool BWD>
@@ -437,19 +462,19 @@ __device__ __forceinline__ void fetch_window(Window<R, CO, C, BWD>& w, uint32_t 
   const uint32_t col_own = (CO - 1) * x.d + x.g * C;
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    const uint32_t o = valid ? ((own + i) * x.W + col_own) * 2u : x.oob_io;
+    const uint32_t o = (valid && x.active) ? ((own + i) * x.W + col_own) * 2u : x.oob_io;
     w.so[i] = load_pack<C>(x.rsc, o);
     w.vo[i] = load_pack<C>(x.rkv, o);
   }
   if constexpr (CO == 2) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const uint32_t o = w.has_prev ? ((own - R + i) * x.W + x.g * C) * 2u : x.oob_io;
+      const uint32_t o = (w.has_prev && x.active) ? ((own - R + i) * x.W + x.g * C) * 2u : x.oob_io;
       w.sp[i] = load_pack<C>(x.rsc, o);
       w.vp[i] = load_pack<C>(x.rkv, o);
     }
   }
-  if constexpr (BWD) w.gd[0] = load_pack<C>(x.rdo, valid ? (n * x.d + x.g * C) * 2u : x.oob_do);
+  if constexpr (BWD) w.gd[0] = load_pack<C>(x.rdo, (valid && x.active) ? (n * x.d + x.g * C) * 2u : x.oob_do);
 }
 
 // ---------------------------------------------------------------------------
@@ -481,6 +506,7 @@ struct WinCtxU {
   uint32_t oob_io, oob_do;
   uint32_t lane_own, lane_prev, lane_gd;  // per-lane byte offsets inside a row
   rsrc_t rkv, rsc, rdo;
+  bool active;                            // the lane's chunk is inside the row
 };
 
 // Fills w for output row n (uniform).  s_hint: a segment index <= the row's
@@ -509,19 +535,22 @@ __device__ __forceinline__ void fetch_window_u(Window<R, CO, C, BWD>& w, uint32_
   w.last = valid && (b + 1 == nb);
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    const uint32_t o = x.lane_own + (valid ? (own + i) * x.row_bytes : x.oob_io);
+    uint32_t o = x.lane_own + (valid ? (own + i) * x.row_bytes : x.oob_io);
+    o = x.active ? o : x.oob_io;
     w.so[i] = load_pack<C>(x.rsc, o);
     w.vo[i] = load_pack<C>(x.rkv, o);
   }
   if constexpr (CO == 2) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const uint32_t o = x.lane_prev + (w.has_prev ? (own - R + i) * x.row_bytes : x.oob_io);
+      uint32_t o = x.lane_prev + (w.has_prev ? (own - R + i) * x.row_bytes : x.oob_io);
+      o = x.active ? o : x.oob_io;
       w.sp[i] = load_pack<C>(x.rsc, o);
       w.vp[i] = load_pack<C>(x.rkv, o);
     }
   }
-  if constexpr (BWD) w.gd[0] = load_pack<C>(x.rdo, x.lane_gd + (valid ? n * x.dout_row_bytes : x.oob_do));
+  if constexpr (BWD)
+    w.gd[0] = load_pack<C>(x.rdo, x.active ? x.lane_gd + (valid ? n * x.dout_row_bytes : x.oob_do) : x.oob_do);
 }
 
 // PF windows in flight along a lane's walk n, n + ns, n + 2 ns, ... < N:
@@ -546,15 +575,16 @@ __device__ __forceinline__ void window_ring(uint32_t n, uint32_t ns, uint32_t N,
 // Forward of one window: the C output columns packed as bf16.
 template <int R, int CO, int C, bool BWD>
 __device__ __forceinline__ Pack<C> fwd_window(const Window<R, CO, C, BWD>& w, const float (&ape_r)[CO][R][C]) {
+  constexpr int NG = kColGroup<C>;
   Pack<C> outp;
   if (CO == 2 && w.has_prev) {
     constexpr int K = 2 * R;
 #pragma unroll
-    for (int kp = 0; kp < C / 2; ++kp) {
-      float x[2][K], v[2][K], e[2][K], Rz[2], o2[2];
+    for (int kp = 0; kp < C / NG; ++kp) {
+      float x[NG][K], v[NG][K], e[NG][K], Rz[NG], o2[NG];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int k = 2 * kp + hh;
+      for (int hh = 0; hh < NG; ++hh) {
+        const int k = NG * kp + hh;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
           x[hh][i] = elem<C>(w.sp[i], k) + ape_r[0][i][k];
@@ -563,24 +593,24 @@ __device__ __forceinline__ Pack<C> fwd_window(const Window<R, CO, C, BWD>& w, co
           v[hh][R + i] = elem<C>(w.vo[i], k);
         }
       }
-      softmax_pool_cols<2, K>(x, v, e, Rz, o2);
-      outp.w[kp] = pack_bf16x2(o2[0], o2[1]);
+      softmax_pool_cols<NG, K>(x, v, e, Rz, o2);
+      outp.w[kp] = pack_group<NG>(o2);
     }
   } else {
 #pragma unroll
-    for (int kp = 0; kp < C / 2; ++kp) {
-      float x[2][R], v[2][R], e[2][R], Rz[2], o2[2];
+    for (int kp = 0; kp < C / NG; ++kp) {
+      float x[NG][R], v[NG][R], e[NG][R], Rz[NG], o2[NG];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int k = 2 * kp + hh;
+      for (int hh = 0; hh < NG; ++hh) {
+        const int k = NG * kp + hh;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
           x[hh][i] = elem<C>(w.so[i], k) + ape_r[CO - 1][i][k];
           v[hh][i] = elem<C>(w.vo[i], k);
         }
       }
-      softmax_pool_cols<2, R>(x, v, e, Rz, o2);
-      outp.w[kp] = pack_bf16x2(o2[0], o2[1]);
+      softmax_pool_cols<NG, R>(x, v, e, Rz, o2);
+      outp.w[kp] = pack_group<NG>(o2);
     }
   }
   return outp;
@@ -589,7 +619,7 @@ __device__ __forceinline__ Pack<C> fwd_window(const Window<R, CO, C, BWD>& w, co
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
-template <int R, int CO, int C, int NT, int TBL, bool UNI, int PF>
+template <int R, int CO, int C, int NT, int TBL, bool UNI, int PF, bool PAD>
 __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
   extern __shared__ int32_t lds[];
   SegTable tab{nullptr, nullptr};
@@ -607,18 +637,22 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
   uint32_t n = L >> lgG;
   if constexpr (UNI) n = __builtin_amdgcn_readfirstlane(n);  // G >= 64: one row per wave
   if (n >= N || nstride == 0) return;
+  // PAD: a row has p.chunks chunks, rounded up to G lanes; the extra lanes
+  // load nothing (past-the-end offsets read 0) and store nothing
+  const bool active = !PAD || g < p.chunks;
 
   const rsrc_t rkv = make_rsrc(p.kv, p.io_bytes);
   const rsrc_t rsc = make_rsrc(p.score, p.io_bytes);
   const rsrc_t rape = make_rsrc(p.ape, R * W * 4u);
   const rsrc_t rout = make_rsrc(p.out, N * d * 2u);
+  const uint32_t oob_out = N * d * 2u;
 
   // APE of this chunk: [half][position][column]
   float ape_r[CO][R][C];
 #pragma unroll
   for (int h = 0; h < CO; ++h)
 #pragma unroll
-    for (int i = 0; i < R; ++i) load_f32<C>(rape, (i * W + h * d + g * C) * 4u, ape_r[h][i]);
+    for (int i = 0; i < R; ++i) load_f32<C>(rape, active ? (i * W + h * d + g * C) * 4u : R * W * 4u, ape_r[h][i]);
 
   if constexpr (UNI) {
     const UTable<TBL> t{p.seg, tab.cu, tab.off};
@@ -635,12 +669,15 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
     x.rkv = rkv;
     x.rsc = rsc;
     x.rdo = rkv;
+    x.active = active;
     const uint32_t lane_out = g * C * 2u, out_row = d * 2u;
     int s_hint = 0;
     using Win = Window<R, CO, C, false>;
     window_ring<PF, Win>(
         n, nstride, N, [&](Win& w, uint32_t m) { fetch_window_u(w, m, s_hint, t, x); },
-        [&](const Win& w, uint32_t m) { store_pack<C>(rout, m * out_row + lane_out, fwd_window(w, ape_r)); });
+        [&](const Win& w, uint32_t m) {
+          store_pack<C>(rout, active ? m * out_row + lane_out : oob_out, fwd_window(w, ape_r));
+        });
   } else {
     WinCtx x;
     x.cu = tab.cu;
@@ -655,11 +692,12 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
     x.rkv = rkv;
     x.rsc = rsc;
     x.rdo = rkv;
+    x.active = active;
     Window<R, CO, C, false> cur, nxt;
     fetch_window(cur, n, x);
     for (; n < N; n += nstride) {
       fetch_window(nxt, n + nstride, x);
-      store_pack<C>(rout, (n * d + g * C) * 2u, fwd_window(cur, ape_r));
+      store_pack<C>(rout, active ? (n * d + g * C) * 2u : oob_out, fwd_window(cur, ape_r));
       cur = nxt;
     }
   }
@@ -670,17 +708,20 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
 // ---------------------------------------------------------------------------
 
 // Zero a byte range [begin, end) of a buffer with 16-byte stores when both
-// ends are 16-byte aligned, 4-byte stores otherwise (rows are a multiple of
-// 4 bytes since coff * head_dim is even).
+// ends are 16-byte aligned, 4-byte stores when both are 4-byte aligned,
+// 2-byte stores otherwise (rows of an odd coff * head_dim).
 __device__ __forceinline__ void zero_range(rsrc_t r, uint32_t begin, uint32_t end, uint32_t first,
                                            uint32_t step) {
   if (((begin | end) & 15u) == 0) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (uint32_t o = begin + first * 16u; o < end; o += step * 16u)
       __builtin_amdgcn_raw_buffer_store_b128(z, r, o, 0, 0);
-  } else {
+  } else if (((begin | end) & 3u) == 0) {
     for (uint32_t o = begin + first * 4u; o < end; o += step * 4u)
       __builtin_amdgcn_raw_buffer_store_b32(0u, r, o, 0, 0);
+  } else {
+    for (uint32_t o = begin + first * 2u; o < end; o += step * 2u)
+      __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(0), r, o, 0, 0);
   }
 }
 
@@ -705,7 +746,7 @@ __device__ void zero_sweep(const BwdParams& p, const SegTable& tab) {
   zero_range(rdsc, b0, b1, zid * NT + threadIdx.x, nz * NT);
 }
 
-template <int R, int CO, int C, int NT, int TBL, bool UNI, int PF>
+template <int R, int CO, int C, int NT, int TBL, bool UNI, int PF, bool PAD>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   extern __shared__ int32_t lds[];
   SegTable tab{nullptr, nullptr};
@@ -748,6 +789,11 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   const rsrc_t rdsc = make_rsrc(p.dscore, p.io_bytes);
   const rsrc_t rape = make_rsrc(p.ape, R * W * 4u);
   const rsrc_t rdo = make_rsrc(p.dout, N * d * 2u);
+  // PAD: a row has p.chunks chunks, rounded up to the lanes of G; the extra
+  // lanes load nothing (past-the-end offsets read 0, so their dAPE terms are
+  // 0) and store nothing
+  const bool active = !PAD || g < p.chunks;
+  auto msk = [&](uint32_t o) { return active ? o : p.io_bytes; };
 
   float ape_r[CO][R][C];
   float acc_r[CO][R][C];
@@ -755,7 +801,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   for (int h = 0; h < CO; ++h)
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      load_f32<C>(rape, (i * W + h * d + g * C) * 4u, ape_r[h][i]);
+      load_f32<C>(rape, active ? (i * W + h * d + g * C) * 4u : R * W * 4u, ape_r[h][i]);
 #pragma unroll
       for (int k = 0; k < C; ++k) acc_r[h][i][k] = 0.0f;
     }
@@ -766,6 +812,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 
   // One window: gradients for its slots, dAPE accumulation, and (segment's
   // last block) the zeros of the never-read slots next to it.
+  constexpr int NG = kColGroup<C>;
   auto body = [&](const Window<R, CO, C, true>& cur) {
     const uint32_t own = cur.own;
     const Pack<C>& gp = cur.gd[0];
@@ -773,12 +820,12 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       constexpr int K = 2 * R;
       Pack<C> gkv[K], gsc[K];
 #pragma unroll
-      for (int kp = 0; kp < C / 2; ++kp) {
-        float a2[2][K], ds2[2][K];
-        float xs[2][K], v[2][K], e[2][K], Rz[2], o2[2];
+      for (int kp = 0; kp < C / NG; ++kp) {
+        float a2[NG][K], ds2[NG][K];
+        float xs[NG][K], v[NG][K], e[NG][K], Rz[NG], o2[NG];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int k = 2 * kp + hh;
+        for (int hh = 0; hh < NG; ++hh) {
+          const int k = NG * kp + hh;
 #pragma unroll
           for (int i = 0; i < R; ++i) {
             xs[hh][i] = elem<C>(cur.sp[i], k) + ape_r[0][i][k];
@@ -787,10 +834,10 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
             v[hh][R + i] = elem<C>(cur.vo[i], k);
           }
         }
-        softmax_pool_cols<2, K>(xs, v, e, Rz, o2);
+        softmax_pool_cols<NG, K>(xs, v, e, Rz, o2);
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int k = 2 * kp + hh;
+        for (int hh = 0; hh < NG; ++hh) {
+          const int k = NG * kp + hh;
           const float Gk = Rz[hh] * elem<C>(gp, k);
 #pragma unroll
           for (int i = 0; i < K; ++i) {
@@ -807,36 +854,36 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         }
 #pragma unroll
         for (int i = 0; i < K; ++i) {
-          gkv[i].w[kp] = pack_bf16x2(a2[0][i], a2[1][i]);
-          gsc[i].w[kp] = pack_bf16x2(ds2[0][i], ds2[1][i]);
+          gkv[i].w[kp] = pack_group_at<NG>(a2, i);
+          gsc[i].w[kp] = pack_group_at<NG>(ds2, i);
         }
       }
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        store_pack<C>(rdkv, (own - R + i) * rowb + lane_prev, gkv[i]);
-        store_pack<C>(rdsc, (own - R + i) * rowb + lane_prev, gsc[i]);
-        store_pack<C>(rdkv, (own + i) * rowb + lane_own, gkv[R + i]);
-        store_pack<C>(rdsc, (own + i) * rowb + lane_own, gsc[R + i]);
+        store_pack<C>(rdkv, msk((own - R + i) * rowb + lane_prev), gkv[i]);
+        store_pack<C>(rdsc, msk((own - R + i) * rowb + lane_prev), gsc[i]);
+        store_pack<C>(rdkv, msk((own + i) * rowb + lane_own), gkv[R + i]);
+        store_pack<C>(rdsc, msk((own + i) * rowb + lane_own), gsc[R + i]);
       }
     } else {
       Pack<C> gkv[R], gsc[R];
 #pragma unroll
-      for (int kp = 0; kp < C / 2; ++kp) {
-        float a2[2][R], ds2[2][R];
-        float xs[2][R], v[2][R], e[2][R], Rz[2], o2[2];
+      for (int kp = 0; kp < C / NG; ++kp) {
+        float a2[NG][R], ds2[NG][R];
+        float xs[NG][R], v[NG][R], e[NG][R], Rz[NG], o2[NG];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int k = 2 * kp + hh;
+        for (int hh = 0; hh < NG; ++hh) {
+          const int k = NG * kp + hh;
 #pragma unroll
           for (int i = 0; i < R; ++i) {
             xs[hh][i] = elem<C>(cur.so[i], k) + ape_r[CO - 1][i][k];
             v[hh][i] = elem<C>(cur.vo[i], k);
           }
         }
-        softmax_pool_cols<2, R>(xs, v, e, Rz, o2);
+        softmax_pool_cols<NG, R>(xs, v, e, Rz, o2);
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int k = 2 * kp + hh;
+        for (int hh = 0; hh < NG; ++hh) {
+          const int k = NG * kp + hh;
           const float Gk = Rz[hh] * elem<C>(gp, k);
 #pragma unroll
           for (int i = 0; i < R; ++i) {
@@ -849,33 +896,33 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         }
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-          gkv[i].w[kp] = pack_bf16x2(a2[0][i], a2[1][i]);
-          gsc[i].w[kp] = pack_bf16x2(ds2[0][i], ds2[1][i]);
+          gkv[i].w[kp] = pack_group_at<NG>(a2, i);
+          gsc[i].w[kp] = pack_group_at<NG>(ds2, i);
         }
       }
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        store_pack<C>(rdkv, (own + i) * rowb + lane_own, gkv[i]);
-        store_pack<C>(rdsc, (own + i) * rowb + lane_own, gsc[i]);
+        store_pack<C>(rdkv, msk((own + i) * rowb + lane_own), gkv[i]);
+        store_pack<C>(rdsc, msk((own + i) * rowb + lane_own), gsc[i]);
       }
     }
     if (cur.last) {
       // The segment's last block owns the never-read slots next to it.
       Pack<C> z;
 #pragma unroll
-      for (int q = 0; q < C / 2; ++q) z.w[q] = 0u;
+      for (int q = 0; q < (C + 1) / 2; ++q) z.w[q] = 0u;
       if (CO == 2) {
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-          store_pack<C>(rdkv, (own + i) * rowb + lane_prev, z);
-          store_pack<C>(rdsc, (own + i) * rowb + lane_prev, z);
+          store_pack<C>(rdkv, msk((own + i) * rowb + lane_prev), z);
+          store_pack<C>(rdsc, msk((own + i) * rowb + lane_prev), z);
         }
       }
       for (uint32_t t = own + R; t < cur.seg_end; ++t) {
 #pragma unroll
         for (int h = 0; h < CO; ++h) {
-          store_pack<C>(rdkv, t * rowb + h * d * 2u + lane_prev, z);
-          store_pack<C>(rdsc, t * rowb + h * d * 2u + lane_prev, z);
+          store_pack<C>(rdkv, msk(t * rowb + h * d * 2u + lane_prev), z);
+          store_pack<C>(rdsc, msk(t * rowb + h * d * 2u + lane_prev), z);
         }
       }
     }
@@ -899,6 +946,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     x.rkv = rkv;
     x.rsc = rsc;
     x.rdo = rdo;
+    x.active = active;
     int s_hint = 0;
     if (n < N && nstride != 0) {
       using Win = Window<R, CO, C, true>;
@@ -920,6 +968,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     x.rkv = rkv;
     x.rsc = rsc;
     x.rdo = rdo;
+    x.active = active;
     Window<R, CO, C, true> cur, nxt;
     fetch_window(cur, n, x);
     for (; n < N && nstride != 0; n += nstride) {
@@ -971,6 +1020,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   for (uint32_t idx = threadIdx.x; idx < CO * R * CW; idx += NT) {
     const uint32_t hi = idx / CW, c = idx - hi * CW;
     const uint32_t h = hi / R, i = hi - h * R;
+    if (PAD && cbase + c >= d) continue;  // padding lanes' columns
     const uint32_t j = i * W + h * d + cbase + c;
     const uint32_t o = ((j / kPartBlock) * prow + wg_in_slice) * kPartBlock + (j % kPartBlock);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(red[idx]), rpart, o * 4u, 0, 0);
@@ -1073,70 +1123,94 @@ __global__ __launch_bounds__(kScanNT) void seg_scan_kernel(SegParams sp, int32_t
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <int R, int CO, int C, bool UNI, int PF>
+template <int R, int CO, int C, bool UNI, int PF, bool PAD>
 static void launch_fwd_rccu(const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
   const dim3 grid(sh.grid), block(kFwdThreads);
   if (p.seg.table == kTableGlobal)
-    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableGlobal, UNI, PF>), grid, block, sh.lds_bytes, st, p);
+    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableGlobal, UNI, PF, PAD>), grid, block, sh.lds_bytes, st, p);
   else if (p.seg.table == kTableArgs)
-    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableArgs, UNI, PF>), grid, block, sh.lds_bytes, st, p);
+    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableArgs, UNI, PF, PAD>), grid, block, sh.lds_bytes, st, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableLds, UNI, PF>), grid, block, sh.lds_bytes, st, p);
+    hipLaunchKernelGGL((fwd_kernel<R, CO, C, kFwdThreads, kTableLds, UNI, PF, PAD>), grid, block, sh.lds_bytes, st, p);
 }
 
 template <int R, int CO, int C>
 static bool launch_fwd_rcc(const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
-  if (!sh.uniform) {
-    launch_fwd_rccu<R, CO, C, false, 2>(p, sh, st);
-    return true;
+  if (sh.pad) {
+    // padded rows (head_dim / cols not a power of two, or one column per
+    // lane): 1 or 2 columns, two windows in flight
+    if constexpr (C <= 2) {
+      if (sh.prefetch != 2) return false;
+      if (sh.uniform)
+        launch_fwd_rccu<R, CO, C, true, 2, true>(p, sh, st);
+      else
+        launch_fwd_rccu<R, CO, C, false, 2, true>(p, sh, st);
+      return true;
+    }
+    return false;
   }
-  switch (sh.prefetch) {
-    case 2: launch_fwd_rccu<R, CO, C, true, 2>(p, sh, st); return true;
-    case 3: launch_fwd_rccu<R, CO, C, true, 3>(p, sh, st); return true;
-    case 4: launch_fwd_rccu<R, CO, C, true, 4>(p, sh, st); return true;
+  if constexpr (C == 1) {
+    return false;
+  } else {
+    if (!sh.uniform) {
+      launch_fwd_rccu<R, CO, C, false, 2, false>(p, sh, st);
+      return true;
+    }
+    switch (sh.prefetch) {
+      case 2: launch_fwd_rccu<R, CO, C, true, 2, false>(p, sh, st); return true;
+      case 3: launch_fwd_rccu<R, CO, C, true, 3, false>(p, sh, st); return true;
+      case 4: launch_fwd_rccu<R, CO, C, true, 4, false>(p, sh, st); return true;
+    }
+    return false;
   }
-  return false;
 }
 
-template <int R, int CO, int C, int NT, bool UNI, int PF>
+template <int R, int CO, int C, int NT, bool UNI, int PF, bool PAD>
 static void launch_bwd_rccnu(const BwdParams& p, const LaunchShape& sh, hipStream_t st) {
   const dim3 grid(sh.grid), block(NT);
   if (p.seg.table == kTableGlobal)
-    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableGlobal, UNI, PF>), grid, block, sh.lds_bytes, st, p);
+    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableGlobal, UNI, PF, PAD>), grid, block, sh.lds_bytes, st, p);
   else if (p.seg.table == kTableArgs)
-    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableArgs, UNI, PF>), grid, block, sh.lds_bytes, st, p);
+    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableArgs, UNI, PF, PAD>), grid, block, sh.lds_bytes, st, p);
   else
-    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableLds, UNI, PF>), grid, block, sh.lds_bytes, st, p);
+    hipLaunchKernelGGL((bwd_kernel<R, CO, C, NT, kTableLds, UNI, PF, PAD>), grid, block, sh.lds_bytes, st, p);
 }
 
 template <int R, int CO, int C, int NT>
 static bool launch_bwd_rccn(const BwdParams& p, const LaunchShape& sh, hipStream_t st) {
-  if (!sh.uniform) {
-    launch_bwd_rccnu<R, CO, C, NT, false, 2>(p, sh, st);
-    return true;
-  }
-  if constexpr (NT <= 512) {
-    switch (sh.prefetch) {
-      case 2: launch_bwd_rccnu<R, CO, C, NT, true, 2>(p, sh, st); return true;
-      case 3: launch_bwd_rccnu<R, CO, C, NT, true, 3>(p, sh, st); return true;
-      case 4: launch_bwd_rccnu<R, CO, C, NT, true, 4>(p, sh, st); return true;
+  if (sh.pad) {
+    // padded rows: 1 or 2 columns, 256 threads, two windows in flight
+    if constexpr (C <= 2 && NT == 256) {
+      if (sh.prefetch != 2) return false;
+      if (sh.uniform)
+        launch_bwd_rccnu<R, CO, C, NT, true, 2, true>(p, sh, st);
+      else
+        launch_bwd_rccnu<R, CO, C, NT, false, 2, true>(p, sh, st);
+      return true;
     }
     return false;
+  }
+  if constexpr (C == 1) {
+    return false;
   } else {
-    // 1024-thread workgroups: deeper rings would not fit the registers
-    if (sh.prefetch != 2) return false;
-    launch_bwd_rccnu<R, CO, C, NT, true, 2>(p, sh, st);
-    return true;
+    if (!sh.uniform) {
+      launch_bwd_rccnu<R, CO, C, NT, false, 2, false>(p, sh, st);
+      return true;
+    }
+    if constexpr (NT <= 512) {
+      switch (sh.prefetch) {
+        case 2: launch_bwd_rccnu<R, CO, C, NT, true, 2, false>(p, sh, st); return true;
+        case 3: launch_bwd_rccnu<R, CO, C, NT, true, 3, false>(p, sh, st); return true;
+        case 4: launch_bwd_rccnu<R, CO, C, NT, true, 4, false>(p, sh, st); return true;
+      }
+      return false;
+    } else {
+      // 1024-thread workgroups: deeper rings would not fit the registers
+      if (sh.prefetch != 2) return false;
+      launch_bwd_rccnu<R, CO, C, NT, true, 2, false>(p, sh, st);
+      return true;
+    }
   }
-}
-
-template <int R, int CO>
-static bool launch_fwd_rc(const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
-  switch (sh.cols) {
-    case 4: return launch_fwd_rcc<R, CO, 4>(p, sh, st);
-    case 2: return launch_fwd_rcc<R, CO, 2>(p, sh, st);
-  }
-  return false;
 }
 
 template <int R, int CO, int C>
@@ -1153,10 +1227,21 @@ static bool launch_bwd_rcc(const BwdParams& p, const LaunchShape& sh, hipStream_
 }
 
 template <int R, int CO>
+static bool launch_fwd_rc(const FwdParams& p, const LaunchShape& sh, hipStream_t st) {
+  switch (sh.cols) {
+    case 4: return launch_fwd_rcc<R, CO, 4>(p, sh, st);
+    case 2: return launch_fwd_rcc<R, CO, 2>(p, sh, st);
+    case 1: return launch_fwd_rcc<R, CO, 1>(p, sh, st);
+  }
+  return false;
+}
+
+template <int R, int CO>
 static bool launch_bwd_rc(const BwdParams& p, const LaunchShape& sh, hipStream_t st) {
   switch (sh.cols) {
     case 4: return launch_bwd_rcc<R, CO, 4>(p, sh, st);
     case 2: return launch_bwd_rcc<R, CO, 2>(p, sh, st);
+    case 1: return launch_bwd_rcc<R, CO, 1>(p, sh, st);
   }
   return false;
 }

@@ -47,7 +47,8 @@ struct FwdParams {
   uint16_t* out;
   uint32_t io_bytes;      // total_tokens * coff * head_dim * 2
   uint32_t head_dim;
-  uint32_t log2_chunks;   // log2(head_dim / cols)
+  uint32_t log2_chunks;   // log2(lanes per row): head_dim / cols rounded up to a power of two
+  uint32_t chunks;        // head_dim / cols (chunks of a row; lanes past it are padding)
 };
 
 struct BwdParams {
@@ -62,7 +63,8 @@ struct BwdParams {
   int32_t* ws_flag;       // validity flag in the workspace
   uint32_t io_bytes;
   uint32_t head_dim;
-  uint32_t log2_chunks;
+  uint32_t log2_chunks;   // log2(lanes per row), as in FwdParams
+  uint32_t chunks;        // head_dim / cols
   uint32_t log2_slice;    // log2(chunks per workgroup column slice)
   uint32_t main_wgs;      // workgroups [0, main_wgs) compute windows, the rest zero-fill
   uint32_t partial_rows;  // main_wgs / slices
@@ -80,8 +82,9 @@ struct ReduceParams {
 struct LaunchShape {
   uint32_t grid;
   uint32_t threads;
-  uint32_t cols;          // output columns per lane (2, 4 or 8)
+  uint32_t cols;          // output columns per lane (1, 2 or 4)
   bool uniform;           // every wave works on one output row at a time
+  bool pad;               // lanes per row rounded up past head_dim / cols (or cols == 1)
   uint32_t prefetch;      // windows in flight per lane (uniform path: 2, 3, 4)
   size_t lds_bytes;
 };

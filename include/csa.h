@@ -84,7 +84,7 @@ typedef enum csa_status {
      * (e.g. total_comp * ratio > total_tokens), an undersized output */
     CSA_STATUS_INVALID_VALUE = 1,
     /* outside the validated envelope: ratio not in {2, 4}, coff not in
-     * {1, 2}, head_dim not a power of two in [2, 1024], or one of
+     * {1, 2}, head_dim not in [1, 1024], or one of
      * (total_tokens+1)*coff*head_dim, total_comp*head_dim,
      * ratio*coff*head_dim not below 2^31 (each checked on its own) */
     CSA_STATUS_NOT_SUPPORTED = 2,

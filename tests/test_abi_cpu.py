@@ -71,8 +71,9 @@ def test_workloads_are_supported(name):
     ((4, 3, 16, 2, 64, 15), G.CsaNotSupported),       # coff 3
     ((2, 0, 16, 2, 64, 15), G.CsaNotSupported),       # coff 0 at ratio 2
     ((2, 3, 16, 2, 64, 15), G.CsaNotSupported),       # coff 3 at ratio 2
-    ((4, 2, 65, 2, 64, 15), G.CsaNotSupported),       # odd head_dim
-    ((4, 2, 96, 2, 64, 15), G.CsaNotSupported),       # not a power of two
+    ((4, 2, 0, 2, 64, 15), G.CsaNotSupported),        # head_dim 0
+    ((4, 2, -8, 2, 64, 15), G.CsaNotSupported),       # negative head_dim
+    ((4, 2, 1025, 2, 64, 15), G.CsaNotSupported),     # beyond 1024
     ((4, 2, 2048, 2, 64, 15), G.CsaNotSupported),     # beyond the launch bound
     ((4, 2, 512, 1, 2 ** 21, 1), G.CsaNotSupported),  # total_tokens*W = 2^31
     ((4, 2, 512, 1, 2 ** 21 - 1, 1), G.CsaNotSupported),  # (total_tokens+1)*W = 2^31
@@ -98,6 +99,14 @@ def test_check_support_size_limits_are_independent():
     G.csa_compressor_check_support(4, 2, 512, 1, 2 ** 21 - 2, 2 ** 18)
     G.csa_compressor_check_support(2, 2, 2, 1, 4, 2)
     G.csa_compressor_check_support(4, 1, 1024, 3, 0, 0)
+
+
+@pytest.mark.parametrize("d", [1, 3, 65, 96, 100, 1000, 1023, 1024])
+def test_any_head_dim_up_to_1024_is_supported(d):
+    for r in (2, 4):
+        for c in (1, 2):
+            G.csa_compressor_check_support(r, c, d, 2, 64, 15)
+            assert G.csa_compressor_bwd_workspace_size(r, c, d, 2, 64, 15) > 0
 
 
 def test_total_comp():
@@ -160,7 +169,7 @@ def test_fwd_rejections_happen_before_any_launch():
     assert _fwd(cu=ctypes.c_void_p(0x200002)) == INV
     assert _fwd(r=3) == NS
     assert _fwd(c=3) == NS
-    assert _fwd(d=24) == NS
+    assert _fwd(d=2048) == NS
     assert _fwd(T=3, N=1) == INV
     # a pack with many segments needs a workspace for its offset table
     assert _fwd(S=5000, T=50000, N=1000) == WS

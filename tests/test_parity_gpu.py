@@ -236,6 +236,44 @@ def test_random_small_packs(dev, case):
     check_against_oracle(cu, T, r, c, d, kv, sc, ape, dout, got)
 
 
+# head_dims outside the power-of-two lane layout: odd (one column per lane,
+# 16-bit accesses) and even with a chunk count that is not a power of two
+# (rows padded to a power of two in lanes); below and above one wave of
+# chunks (per-lane and wave-uniform paths)
+ODD_DIMS = [1, 3, 7, 33, 65, 127, 129, 255, 1023]
+EVEN_NONPOW2_DIMS = [6, 12, 96, 100, 192, 258, 320, 1000]
+
+
+def _nonpow2_cases():
+    rng = np.random.default_rng(2024)
+    cases = []
+    for i, d in enumerate(ODD_DIMS + EVEN_NONPOW2_DIMS):
+        nseg = int(rng.integers(1, 6))
+        lengths = rng.integers(0, 90, size=nseg).tolist()
+        lengths[int(rng.integers(0, nseg))] = int(rng.integers(1, 4))  # a segment shorter than ratio
+        T = int(sum(lengths)) + int(rng.integers(1, 12))           # with padding rows
+        r = int(rng.choice([2, 4]))
+        c = int(rng.choice([1, 2]))
+        cases.append((lengths, T, r, c, d, 500 + i))
+    # every (ratio, coff) at one odd and one padded head_dim
+    for j, (r, c) in enumerate([(2, 1), (2, 2), (4, 1), (4, 2)]):
+        for d in (65, 192):
+            cases.append(([37, 0, 130, 5, 64], 250, r, c, d, 700 + 10 * j + d))
+    return cases
+
+
+@pytest.mark.parametrize("case", _nonpow2_cases(), ids=lambda c: f"d{c[4]}_r{c[2]}_c{c[3]}_s{c[5]}")
+def test_non_power_of_two_head_dims(dev, case):
+    lengths, T, r, c, d, seed = case
+    wl = inputs.custom("np2", lengths, T, r, c, d, seed=seed)
+    cu = list(wl.cu_seqlens)
+    N = G.csa_compressor_total_comp(cu, r)
+    kv, sc, ape, dout = inputs.make_tensors(wl, N)
+    for host in (True, False):
+        got = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N, host=host)
+        check_against_oracle(cu, T, r, c, d, kv, sc, ape, dout, got)
+
+
 def test_extreme_scores_and_subnormals(dev):
     """Score spreads that push EXP to its clamp and products into fp32
     subnormals: still bit-identical (IEEE subnormals on both sides)."""

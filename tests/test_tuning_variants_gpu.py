@@ -46,4 +46,4 @@ def test_tuning_variant_parity(gpu, knobs):
     p = subprocess.run([sys.executable, "-u", "-m", "tests.tuning_parity"], cwd=ROOT, env=env,
                        capture_output=True, text=True, timeout=240)
     assert p.returncode == 0, f"{knobs}: rc {p.returncode}\n{p.stdout[-2000:]}\n{p.stderr[-3000:]}"
-    assert p.stdout.count("ok ") == 7, p.stdout
+    assert p.stdout.count("ok ") == 9, p.stdout

@@ -30,6 +30,9 @@ def cases():
     rng = np.random.default_rng(77)
     lengths = rng.integers(0, 300, size=60).tolist()   # 60 segments: LDS table
     yield "random60_d256_r2_c2", inputs.custom("r60", lengths, int(sum(lengths)) + 5, 2, 2, 256, seed=3), True
+    lengths = rng.integers(0, 200, size=9).tolist()    # padded rows (96 = 48 chunks of 2) and odd d
+    yield "random9_d96_r4_c2", inputs.custom("r9", lengths, int(sum(lengths)) + 3, 4, 2, 96, seed=6), True
+    yield "random9_d65_r2_c1", inputs.custom("r9b", lengths, int(sum(lengths)) + 3, 2, 1, 65, seed=7), False
     lengths = rng.integers(0, 12, size=2500).tolist()  # above the LDS table limit: workspace table
     yield "random2500_d128_r4_c2", inputs.custom("r2500", lengths, int(sum(lengths)) + 9, 4, 2, 128, seed=4), False
 
