@@ -256,7 +256,7 @@ Plan make_plan(const Problem& p) {
     pl.bwd_main_wgs = static_cast<uint32_t>(main);
     pl.partial_rows = static_cast<uint32_t>(main / slices);
     pl.lds_table_words = pl.global_table ? 0 : static_cast<uint32_t>(2 * (NT / 64) + 2 * (p.S + 1));
-    const uint64_t red_floats = uint64_t(p.coff) * p.ratio * CS * C;
+    const uint64_t red_floats = uint64_t(NT) * p.coff * p.ratio * C;  // dAPE staging: every thread's sums
     pl.bwd.lds_bytes = (uint64_t(pl.lds_table_words) + red_floats) * 4;
     pl.partial_offset = kHeaderBytes + pl.off_bytes;
     const uint64_t nblk = (uint64_t(p.ratio) * W + csa::kPartBlock - 1) / csa::kPartBlock;

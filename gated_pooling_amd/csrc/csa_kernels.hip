@@ -30,9 +30,9 @@
 //     the segment's seqlen % ratio tail rows; extra "zero" workgroups write
 //     the rows of segments shorter than ratio and the rows past cu[S].
 //   * dAPE: per-lane fp32 accumulators, reduced in a fixed order inside the
-//     workgroup (butterfly shuffles, then waves in index order through LDS),
-//     one partial row per workgroup in the workspace, then a second kernel
-//     sums the partial rows in a fixed order.  Deterministic.
+//     workgroup (staged in LDS, summed over the workgroup's row groups in
+//     order), one partial row per workgroup in the workspace, then a second
+//     kernel sums the partial rows in a fixed order.  Deterministic.
 //   * The cu_seqlens -> output-block offset scan runs in each workgroup's
 //     prologue (LDS) for up to kMaxLdsSegments segments; larger packs use a
 //     one-workgroup scan kernel writing the offsets to the workspace; small
@@ -979,36 +979,26 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   }
 
   // ---- dAPE: fixed-order reduction inside the workgroup ----
-  // 1) lanes of a wave that share a chunk (CS < 64): xor butterfly.
-  if (CS < 64) {
-    for (uint32_t o = CS; o < 64; o <<= 1) {
-#pragma unroll
-      for (int h = 0; h < CO; ++h)
-#pragma unroll
-        for (int i = 0; i < R; ++i)
-#pragma unroll
-          for (int k = 0; k < C; ++k) acc_r[h][i][k] += __shfl_xor(acc_r[h][i][k], o, 64);
-    }
-  }
-  // 2) waves in index order into LDS red[h][i][c], c over the slice's CS*C
-  //    columns (per half).
+  // Every thread stages its CO*R*C sums in LDS at stage[rg][h][i][gl*C + k]
+  // (rg: the thread's row group, gl: its chunk in the slice).  After one
+  // barrier, value q of the slice is the sum over row groups rg = 0, 1, ...
+  // in that order (one barrier and no read-modify-write rounds: the tail
+  // runs when every workgroup finishes at once, so it is on the critical
+  // path).
   const uint32_t CW = CS * C;
-  float* red = reinterpret_cast<float*>(lds + p.lds_table_words);
-  for (uint32_t idx = threadIdx.x; idx < CO * R * CW; idx += NT) red[idx] = 0.0f;
-  __syncthreads();
-  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t gl = threadIdx.x & (CS - 1);
-  for (uint32_t w = 0; w < NT / 64; ++w) {
-    if (wave == w && (CS >= 64 || lane < CS)) {
+  const uint32_t RG = NT >> lgCS;   // row groups of the workgroup
+  const uint32_t QW = CO * R * CW;  // values of one row group
+  float* stage = reinterpret_cast<float*>(lds + p.lds_table_words);
+  {
+    const uint32_t rg = threadIdx.x >> lgCS, gl = threadIdx.x & (CS - 1);
 #pragma unroll
-      for (int h = 0; h < CO; ++h)
+    for (int h = 0; h < CO; ++h)
 #pragma unroll
-        for (int i = 0; i < R; ++i)
+      for (int i = 0; i < R; ++i)
 #pragma unroll
-          for (int k = 0; k < C; ++k) red[(h * R + i) * CW + gl * C + k] += acc_r[h][i][k];
-    }
-    __syncthreads();
+        for (int k = 0; k < C; ++k) stage[rg * QW + (h * R + i) * CW + gl * C + k] = acc_r[h][i][k];
   }
+  __syncthreads();
   // 3) one partial row per workgroup of a slice, stored in column blocks of
   //    kPartBlock floats: value j = i*W + h*d + col of partial row `row` is at
   //    ((j / kPartBlock) * rows + row) * kPartBlock + j % kPartBlock, so the
@@ -1017,13 +1007,15 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   const uint32_t prow = p.partial_rows;
   const uint32_t nblk = (R * W + kPartBlock - 1) / kPartBlock;
   const rsrc_t rpart = make_rsrc(p.partials, nblk * prow * kPartBlock * 4u);
-  for (uint32_t idx = threadIdx.x; idx < CO * R * CW; idx += NT) {
+  for (uint32_t idx = threadIdx.x; idx < QW; idx += NT) {
     const uint32_t hi = idx / CW, c = idx - hi * CW;
     const uint32_t h = hi / R, i = hi - h * R;
     if (PAD && cbase + c >= d) continue;  // padding lanes' columns
+    float t = stage[idx];
+    for (uint32_t g2 = 1; g2 < RG; ++g2) t = t + stage[g2 * QW + idx];
     const uint32_t j = i * W + h * d + cbase + c;
     const uint32_t o = ((j / kPartBlock) * prow + wg_in_slice) * kPartBlock + (j % kPartBlock);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(red[idx]), rpart, o * 4u, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(t), rpart, o * 4u, 0, 0);
   }
 }
 
