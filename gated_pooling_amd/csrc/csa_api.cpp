@@ -7,7 +7,8 @@
 //
 // Support envelope ([PR5984] = NVIDIA/Megatron-LM pull request 5984 page,
 // [PR710] = cudnn-frontend pull request 710 page): ratio in {2, 4}
-// ([PR710: What]), coff in {1, 2} ([PR5984: coff commit]); the size limits
+// ([PR710: What]) and 128 with head_dim a multiple of 64 ([PR5984: ratio=128
+// commit]), coff in {1, 2} ([PR5984: coff commit]); the size limits
 // total_tokens*coff*head_dim, total_comp*head_dim and ratio*coff*head_dim
 // below 2^31 each, and the rejection of total_comp > 0 with
 // total_tokens < ratio ([PR5984: review-feedback commit; PR710: What]).
@@ -69,6 +70,8 @@ struct Tuning {
   int uniform = 1;        // wave-uniform row path where a row has >= 64 chunks
   int fwd_prefetch = 2;   // windows in flight per lane (uniform path)
   int bwd_prefetch = 3;
+  int r128_fwd_wgs = 512; // ratio 128 grid caps (workgroups)
+  int r128_bwd_wgs = 256;
 };
 
 int env_int(const char* name, int dflt, const int* allowed, int n_allowed, int lo, int hi) {
@@ -99,6 +102,8 @@ const Tuning& tuning() {
     d.uniform = env_int("CSA_UNIFORM", d.uniform, nullptr, 0, 0, 1);
     d.fwd_prefetch = env_int("CSA_FWD_PREFETCH", d.fwd_prefetch, nullptr, 0, 2, 4);
     d.bwd_prefetch = env_int("CSA_BWD_PREFETCH", d.bwd_prefetch, nullptr, 0, 2, 4);
+    d.r128_fwd_wgs = env_int("CSA_R128_FWD_WGS", d.r128_fwd_wgs, nullptr, 0, 1, 1 << 20);
+    d.r128_bwd_wgs = env_int("CSA_R128_BWD_WGS", d.r128_bwd_wgs, nullptr, 0, 1, 1 << 16);
     return d;
   }();
   return t;
@@ -118,12 +123,15 @@ int log2i(int64_t x) {
 uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
 csa_status_t check_problem(const Problem& p) {
-  if (p.ratio != 2 && p.ratio != 4)
-    return fail(CSA_STATUS_NOT_SUPPORTED, "ratio must be 2 or 4 (got %d)", p.ratio);
+  if (p.ratio != 2 && p.ratio != 4 && p.ratio != csa::kRatio128)
+    return fail(CSA_STATUS_NOT_SUPPORTED, "ratio must be 2, 4 or 128 (got %d)", p.ratio);
   if (p.coff != 1 && p.coff != 2)
     return fail(CSA_STATUS_NOT_SUPPORTED, "coff must be 1 or 2 (got %d)", p.coff);
   if (p.head_dim < 1 || p.head_dim > 1024)
     return fail(CSA_STATUS_NOT_SUPPORTED, "head_dim must be in [1, 1024] (got %d)", p.head_dim);
+  if (p.ratio == csa::kRatio128 && p.head_dim % csa::kSlice128 != 0)
+    return fail(CSA_STATUS_NOT_SUPPORTED, "ratio 128 needs head_dim a multiple of %d (got %d)", csa::kSlice128,
+                p.head_dim);
   if (p.S < 0 || p.T < 0 || p.N < 0)
     return fail(CSA_STATUS_INVALID_VALUE, "negative size: num_segments=%d total_tokens=%lld total_comp=%lld",
                 p.S, (long long)p.T, (long long)p.N);
@@ -168,6 +176,9 @@ struct Plan {
   uint32_t lds_table_words;
   uint64_t partial_offset;
   uint64_t ws_bwd;
+  // ratio 128
+  uint32_t nslices;
+  uint32_t fwd_lds_table_words;
 };
 
 constexpr uint64_t kHeaderBytes = 256;
@@ -185,7 +196,65 @@ int64_t pow2_ceil(int64_t x) {
   return p;
 }
 
+// ratio 128: a workgroup per (column slice, group of output rows), the
+// window slice staged in LDS (see the kernels).  Grids are capped at the
+// number of workgroups the chip holds at once.
+Plan make_plan_r128(const Problem& p) {
+  const Tuning& tu = tuning();
+  Plan pl{};
+  const int64_t W = int64_t{p.coff} * p.head_dim;
+  pl.global_table = p.S > csa::kMaxLdsSegments;
+  pl.off_bytes = pl.global_table ? align_up(uint64_t(p.S + 1) * 4, 256) : 0;
+  const int NT = p.coff * 128;                       // one wave per 64-entry chunk
+  const int chunks = p.coff * 2;
+  const uint64_t stage_bytes = 2ull * p.coff * csa::kRatio128 * csa::kSlice128 * 2;
+  const uint64_t red_bytes = 3ull * chunks * 64 * 4;
+  // the staged window follows the table in LDS and is accessed 16 bytes at a
+  // time: keep it 16-byte aligned
+  const uint32_t table_words =
+      pl.global_table ? 0 : static_cast<uint32_t>(align_up(2 * (NT / 64) + 2 * uint64_t(p.S + 1), 4));
+  pl.nslices = static_cast<uint32_t>(p.head_dim / csa::kSlice128);
+  const int64_t rows = p.N > 0 ? p.N : 1;
+  {
+    int64_t per = tu.r128_fwd_wgs / pl.nslices;
+    if (per < 1) per = 1;
+    if (per > rows) per = rows;
+    pl.fwd.grid = static_cast<uint32_t>(per * pl.nslices);
+    pl.fwd.threads = NT;
+    pl.fwd.cols = 1;
+    pl.fwd_lds_table_words = table_words;
+    pl.fwd.lds_bytes = table_words * 4ull + stage_bytes + red_bytes;
+    pl.ws_fwd = pl.global_table ? kHeaderBytes + pl.off_bytes : 0;
+  }
+  {
+    int64_t per = tu.r128_bwd_wgs / pl.nslices;
+    if (per < 1) per = 1;
+    if (per > rows) per = rows;
+    const int64_t main = per * pl.nslices;
+    const int64_t spare_rows = p.T - p.N * p.ratio;
+    int64_t zero = 0;
+    if (spare_rows > 0) {
+      const int64_t bytes = spare_rows * W * 2 * 2;
+      zero = (bytes + int64_t{NT} * 16 * 8 - 1) / (int64_t{NT} * 16 * 8);
+      if (zero < 1) zero = 1;
+      if (zero > 256) zero = 256;
+    }
+    pl.bwd.grid = static_cast<uint32_t>(main + zero);
+    pl.bwd.threads = NT;
+    pl.bwd.cols = 1;
+    pl.bwd_main_wgs = static_cast<uint32_t>(main);
+    pl.partial_rows = static_cast<uint32_t>(per);
+    pl.lds_table_words = table_words;
+    pl.bwd.lds_bytes = table_words * 4ull + stage_bytes + red_bytes;
+    pl.partial_offset = kHeaderBytes + pl.off_bytes;
+    const uint64_t nblk = (uint64_t(p.ratio) * W + csa::kPartBlock - 1) / csa::kPartBlock;
+    pl.ws_bwd = pl.partial_offset + align_up(nblk * pl.partial_rows * csa::kPartBlock * 4, 256);
+  }
+  return pl;
+}
+
 Plan make_plan(const Problem& p) {
+  if (p.ratio == csa::kRatio128) return make_plan_r128(p);
   const Tuning& tu = tuning();
   Plan pl{};
   const int64_t W = int64_t{p.coff} * p.head_dim;
@@ -359,6 +428,27 @@ csa_status_t launch_bwd_grads(const Problem& pr, const Plan& pl, const void* kv,
                               void* dkv, void* dscore, void* workspace, hipStream_t stream) {
   csa_status_t st = launch_scan_if_needed(pr, pl, cu, workspace, stream);
   if (st) return st;
+  if (pr.ratio == csa::kRatio128) {
+    csa::Bwd128Params bp{};
+    bp.seg = seg_params(pr, pl, cu, cu_host, workspace);
+    bp.kv = static_cast<const uint16_t*>(kv);
+    bp.score = static_cast<const uint16_t*>(score);
+    bp.ape = ape;
+    bp.dout = static_cast<const uint16_t*>(dout);
+    bp.dkv = static_cast<uint16_t*>(dkv);
+    bp.dscore = static_cast<uint16_t*>(dscore);
+    bp.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.partial_offset);
+    bp.ws_flag = reinterpret_cast<int32_t*>(workspace);
+    bp.io_bytes = static_cast<uint32_t>(pr.T * pr.coff * pr.head_dim * 2);
+    bp.head_dim = pr.head_dim;
+    bp.nslices = pl.nslices;
+    bp.main_wgs = pl.bwd_main_wgs;
+    bp.partial_rows = pl.partial_rows;
+    bp.lds_table_words = pl.lds_table_words;
+    if (!csa::launch_bwd128(pr.coff, bp, pl.bwd.grid, pl.bwd.lds_bytes, stream))
+      return fail(CSA_STATUS_NOT_SUPPORTED, "no ratio-128 backward kernel for this configuration");
+    return after_launch("backward");
+  }
   csa::BwdParams bp{};
   bp.seg = seg_params(pr, pl, cu, cu_host, workspace);
   bp.kv = static_cast<const uint16_t*>(kv);
@@ -473,6 +563,21 @@ csa_status_t csa_compressor_fwd(const void* kv, const void* score, const float* 
   if (pl.ws_fwd > 0 && (st = check_ptr(workspace, "workspace"))) return st;
 
   if ((st = launch_scan_if_needed(pr, pl, cu, workspace, stream))) return st;
+  if (ratio == csa::kRatio128) {
+    csa::Fwd128Params fp{};
+    fp.seg = seg_params(pr, pl, cu, cu_host, workspace);
+    fp.kv = static_cast<const uint16_t*>(kv);
+    fp.score = static_cast<const uint16_t*>(score);
+    fp.ape = ape;
+    fp.out = static_cast<uint16_t*>(out);
+    fp.io_bytes = static_cast<uint32_t>(pr.T * pr.coff * pr.head_dim * 2);
+    fp.head_dim = head_dim;
+    fp.nslices = pl.nslices;
+    fp.lds_table_words = pl.fwd_lds_table_words;
+    if (!csa::launch_fwd128(coff, fp, pl.fwd.grid, pl.fwd.lds_bytes, stream))
+      return fail(CSA_STATUS_NOT_SUPPORTED, "no ratio-128 forward kernel for this configuration");
+    return after_launch("forward");
+  }
   csa::FwdParams fp{};
   fp.seg = seg_params(pr, pl, cu, cu_host, workspace);
   fp.kv = static_cast<const uint16_t*>(kv);

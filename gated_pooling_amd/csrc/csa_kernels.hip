@@ -725,8 +725,8 @@ __device__ __forceinline__ void zero_range(rsrc_t r, uint32_t begin, uint32_t en
   }
 }
 
-template <int R, int CO, int NT>
-__device__ void zero_sweep(const BwdParams& p, const SegTable& tab) {
+template <int R, int CO, int NT, typename Params>
+__device__ void zero_sweep(const Params& p, const SegTable& tab) {
   const uint32_t W = CO * p.head_dim, row_bytes = W * 2u;
   const rsrc_t rdkv = make_rsrc(p.dkv, p.io_bytes);
   const rsrc_t rdsc = make_rsrc(p.dscore, p.io_bytes);
@@ -1076,6 +1076,308 @@ __global__ __launch_bounds__(kReduceNT) void dape_reduce_kernel(ReduceParams p) 
 }
 
 // ---------------------------------------------------------------------------
+// ratio = 128 [PR5984: ratio=128 commit]: a window holds 128 * coff rows per
+// column, too many for registers.  A workgroup owns a slice of kSlice128
+// columns (lane = column) and walks output rows; per row:
+//   1. the window's row slices (score and kv, 128 bytes each) are staged in
+//      LDS with 16-byte loads;
+//   2. wave w takes window entries [64w, 64w + 64) (one summation chunk):
+//      x_k = score + ape, the chunk max, exchanged through LDS -> window max m;
+//   3. e_k = EXP(x_k - m), the chunk's Z (from its first e) and acc (fma chain
+//      from 0), merged in chunk order through LDS: exactly the chunked fp32
+//      order of windows above 64 entries (the first block at coff 2 has only
+//      the own half: chunks 2 and 3);
+//   backward 4. a_k = e_k * R * g, ds_k = a_k (v_k - o), bf16 results written
+//      over the staged inputs in LDS, then stored with 16-byte stores; dAPE
+//      sums stay in registers (a wave always holds the same 64 positions of
+//      its slice) and leave as one partial row per workgroup.
+// head_dim is a multiple of kSlice128, so every row slice is whole.
+// ---------------------------------------------------------------------------
+template <int CO>
+struct Win128 {
+  static constexpr int kRows = CO * kRatio128;        // window rows
+  static constexpr int kChunks = kRows / kChunk128;   // summation chunks (= waves)
+  static constexpr int kThreads = kChunks * 64;
+  static constexpr int kStageBytes = 2 * kRows * kSlice128 * 2;  // score, kv as bf16
+};
+
+// Byte offset in kv/score of window row k's slice, or `oob` when the row is
+// masked (the previous half of a segment's first block).
+template <int CO>
+__device__ __forceinline__ uint32_t row128_offset(int k, uint32_t own, bool has_prev, uint32_t row_bytes,
+                                                  uint32_t half_bytes, uint32_t slice_bytes, uint32_t oob) {
+  if constexpr (CO == 2) {
+    if (k < kRatio128) return has_prev ? (own - kRatio128 + k) * row_bytes + slice_bytes : oob;
+    return (own + k - kRatio128) * row_bytes + half_bytes + slice_bytes;
+  } else {
+    return (own + k) * row_bytes + slice_bytes;
+  }
+}
+
+// Row of output row n (uniform): segment lookup on the scalar unit.
+struct Row128 {
+  uint32_t own, seg_end;
+  bool has_prev, last;
+};
+template <int TBL>
+__device__ __forceinline__ Row128 row128(uint32_t n, int& s_hint, const UTable<TBL>& t, int S) {
+  int lo = s_hint, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (t.off_at(mid) <= n) lo = mid; else hi = mid - 1;
+  }
+  s_hint = lo;
+  const uint32_t o0 = t.off_at(lo), b = n - o0, nb = t.off_at(lo + 1) - o0;
+  Row128 r;
+  r.own = t.cu_at(lo) + b * kRatio128;
+  r.seg_end = t.cu_at(lo + 1);
+  r.has_prev = b > 0;
+  r.last = b + 1 == nb;
+  return r;
+}
+
+// Stage the window's score and kv slices in LDS: stage[tensor][k][64] bf16.
+template <int CO>
+__device__ __forceinline__ void stage_window128(uint16_t* stage, rsrc_t rsc, rsrc_t rkv, const Row128& row,
+                                                uint32_t row_bytes, uint32_t half_bytes, uint32_t slice_bytes,
+                                                uint32_t oob) {
+  using Wn = Win128<CO>;
+  constexpr int kParts = kSlice128 * 2 / 16;  // 16-byte parts of a row slice
+  for (int q = threadIdx.x; q < 2 * Wn::kRows * kParts; q += Wn::kThreads) {
+    const int part = q % kParts, rq = q / kParts;
+    const int tensor = rq / Wn::kRows, k = rq % Wn::kRows;
+    const uint32_t o = row128_offset<CO>(k, row.own, CO == 2 && row.has_prev, row_bytes, half_bytes, slice_bytes, oob);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(tensor ? rkv : rsc, o == oob ? oob : o + part * 16u, 0,
+                                                          kAuxStream);
+    *reinterpret_cast<u32x4*>(stage + (tensor * Wn::kRows + k) * kSlice128 + part * 8) = v;
+  }
+}
+
+template <int CO, int TBL>
+__global__ __launch_bounds__(Win128<CO>::kThreads) void fwd128_kernel(Fwd128Params p) {
+  using Wn = Win128<CO>;
+  constexpr int NT = Wn::kThreads;
+  extern __shared__ int32_t lds[];
+  SegTable tab{nullptr, nullptr};
+  if constexpr (TBL != kTableArgs) {
+    if (!load_segment_table<kRatio128, NT, TBL>(p.seg, lds, tab)) return;
+  }
+  uint16_t* stage = reinterpret_cast<uint16_t*>(lds + p.lds_table_words);
+  float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(stage) + Wn::kStageBytes);  // [3][kChunks][64]
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t d = p.head_dim, W = CO * d, N = static_cast<uint32_t>(p.seg.N);
+  const uint32_t nslices = p.nslices, slice = blockIdx.x % nslices, per_slice = gridDim.x / nslices;
+  const uint32_t col = slice * kSlice128 + lane;
+  const uint32_t half = (CO == 2) ? (wave >> 1) : 0;   // the chunk's half of the row
+  const uint32_t pos0 = (wave & 1) * kChunk128;        // its first position in the block
+  const rsrc_t rkv = make_rsrc(p.kv, p.io_bytes);
+  const rsrc_t rsc = make_rsrc(p.score, p.io_bytes);
+  const rsrc_t rape = make_rsrc(p.ape, kRatio128 * W * 4u);
+  const rsrc_t rout = make_rsrc(p.out, N * d * 2u);
+  float ape_r[kChunk128];
+#pragma unroll
+  for (int k = 0; k < kChunk128; ++k)
+    ape_r[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rape, ((pos0 + k) * W + half * d + col) * 4u, 0, 0));
+
+  const UTable<TBL> t{p.seg, tab.cu, tab.off};
+  int s_hint = 0;
+  const uint32_t row_bytes = W * 2u, half_bytes = d * 2u, slice_bytes = slice * kSlice128 * 2u;
+  for (uint32_t n = __builtin_amdgcn_readfirstlane(blockIdx.x / nslices); n < N; n += per_slice) {
+    const Row128 row = row128<TBL>(n, s_hint, t, p.seg.S);
+    stage_window128<CO>(stage, rsc, rkv, row, row_bytes, half_bytes, slice_bytes, p.io_bytes);
+    __syncthreads();
+    const bool present = !(CO == 2 && wave < 2 && !row.has_prev);
+    const uint16_t* ss = stage + (wave * kChunk128) * kSlice128 + lane;
+    const uint16_t* sv = stage + (Wn::kRows + wave * kChunk128) * kSlice128 + lane;
+    float x[kChunk128];
+    float m = 0.0f;
+    if (present) {
+#pragma unroll
+      for (int k = 0; k < kChunk128; ++k) x[k] = __uint_as_float(uint32_t(ss[k * kSlice128]) << 16) + ape_r[k];
+      m = x[0];
+#pragma unroll
+      for (int k = 1; k < kChunk128; ++k) m = fmaxf(m, x[k]);
+    }
+    const int first = (CO == 2 && !row.has_prev) ? 2 : 0;
+    red[wave * 64 + lane] = m;
+    __syncthreads();
+    m = red[first * 64 + lane];
+    for (int w = first + 1; w < Wn::kChunks; ++w) m = fmaxf(m, red[w * 64 + lane]);
+    float zc = 0.0f, ac = 0.0f;
+    if (present) {
+      float e[kChunk128];
+#pragma unroll
+      for (int k = 0; k < kChunk128; ++k) e[k] = csa_exp(x[k] - m);
+      zc = e[0];
+#pragma unroll
+      for (int k = 1; k < kChunk128; ++k) zc = zc + e[k];
+#pragma unroll
+      for (int k = 0; k < kChunk128; ++k) ac = __builtin_fmaf(e[k], __uint_as_float(uint32_t(sv[k * kSlice128]) << 16), ac);
+    }
+    red[(Wn::kChunks + wave) * 64 + lane] = zc;
+    red[(2 * Wn::kChunks + wave) * 64 + lane] = ac;
+    __syncthreads();
+    if (wave == 0) {
+      float Z = red[(Wn::kChunks + first) * 64 + lane], acc = red[(2 * Wn::kChunks + first) * 64 + lane];
+      for (int w = first + 1; w < Wn::kChunks; ++w) {
+        Z = Z + red[(Wn::kChunks + w) * 64 + lane];
+        acc = acc + red[(2 * Wn::kChunks + w) * 64 + lane];
+      }
+      const float o = acc * (1.0f / Z);
+      const Pack<1> ob{{pack_bf16x2(o, 0.0f)}};
+      store_pack<1>(rout, (n * d + col) * 2u, ob);
+    }
+    __syncthreads();  // the next row's staging overwrites stage and red
+  }
+}
+
+template <int CO, int TBL>
+__global__ __launch_bounds__(Win128<CO>::kThreads) void bwd128_kernel(Bwd128Params p) {
+  using Wn = Win128<CO>;
+  constexpr int NT = Wn::kThreads;
+  extern __shared__ int32_t lds[];
+  SegTable tab{nullptr, nullptr};
+  bool valid = true;
+  if constexpr (TBL == kTableArgs) {
+    if (blockIdx.x >= p.main_wgs) load_segment_table<kRatio128, NT, TBL>(p.seg, lds, tab);
+  } else {
+    valid = load_segment_table<kRatio128, NT, TBL>(p.seg, lds, tab);
+  }
+  if (TBL != kTableGlobal && blockIdx.x == 0 && threadIdx.x == 0) __builtin_nontemporal_store(valid ? 1 : 0, p.ws_flag);
+  if (!valid) return;
+  if (blockIdx.x >= p.main_wgs) {
+    zero_sweep<kRatio128, CO, NT>(p, tab);
+    return;
+  }
+  uint16_t* stage = reinterpret_cast<uint16_t*>(lds + p.lds_table_words);
+  float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(stage) + Wn::kStageBytes);
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t d = p.head_dim, W = CO * d, N = static_cast<uint32_t>(p.seg.N);
+  const uint32_t nslices = p.nslices, slice = blockIdx.x % nslices, per_slice = p.main_wgs / nslices;
+  const uint32_t wg_in_slice = blockIdx.x / nslices;
+  const uint32_t col = slice * kSlice128 + lane;
+  const uint32_t half = (CO == 2) ? (wave >> 1) : 0;
+  const uint32_t pos0 = (wave & 1) * kChunk128;
+  const rsrc_t rkv = make_rsrc(p.kv, p.io_bytes);
+  const rsrc_t rsc = make_rsrc(p.score, p.io_bytes);
+  const rsrc_t rdkv = make_rsrc(p.dkv, p.io_bytes);
+  const rsrc_t rdsc = make_rsrc(p.dscore, p.io_bytes);
+  const rsrc_t rape = make_rsrc(p.ape, kRatio128 * W * 4u);
+  const rsrc_t rdo = make_rsrc(p.dout, N * d * 2u);
+  float ape_r[kChunk128], dape_r[kChunk128];
+#pragma unroll
+  for (int k = 0; k < kChunk128; ++k) {
+    ape_r[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rape, ((pos0 + k) * W + half * d + col) * 4u, 0, 0));
+    dape_r[k] = 0.0f;
+  }
+
+  const UTable<TBL> t{p.seg, tab.cu, tab.off};
+  int s_hint = 0;
+  const uint32_t row_bytes = W * 2u, half_bytes = d * 2u, slice_bytes = slice * kSlice128 * 2u;
+  constexpr int kParts = kSlice128 * 2 / 16;
+  for (uint32_t n = __builtin_amdgcn_readfirstlane(wg_in_slice); n < N; n += per_slice) {
+    const Row128 row = row128<TBL>(n, s_hint, t, p.seg.S);
+    stage_window128<CO>(stage, rsc, rkv, row, row_bytes, half_bytes, slice_bytes, p.io_bytes);
+    const float g = elem<1>(load_pack<1>(rdo, (n * d + col) * 2u), 0);
+    __syncthreads();
+    const bool present = !(CO == 2 && wave < 2 && !row.has_prev);
+    uint16_t* ss = stage + (wave * kChunk128) * kSlice128 + lane;
+    uint16_t* sv = stage + (Wn::kRows + wave * kChunk128) * kSlice128 + lane;
+    float e[kChunk128];
+    float m = 0.0f;
+    if (present) {
+#pragma unroll
+      for (int k = 0; k < kChunk128; ++k) e[k] = __uint_as_float(uint32_t(ss[k * kSlice128]) << 16) + ape_r[k];
+      m = e[0];
+#pragma unroll
+      for (int k = 1; k < kChunk128; ++k) m = fmaxf(m, e[k]);
+    }
+    const int first = (CO == 2 && !row.has_prev) ? 2 : 0;
+    red[wave * 64 + lane] = m;
+    __syncthreads();
+    m = red[first * 64 + lane];
+    for (int w = first + 1; w < Wn::kChunks; ++w) m = fmaxf(m, red[w * 64 + lane]);
+    float zc = 0.0f, ac = 0.0f;
+    if (present) {
+#pragma unroll
+      for (int k = 0; k < kChunk128; ++k) e[k] = csa_exp(e[k] - m);
+      zc = e[0];
+#pragma unroll
+      for (int k = 1; k < kChunk128; ++k) zc = zc + e[k];
+#pragma unroll
+      for (int k = 0; k < kChunk128; ++k) ac = __builtin_fmaf(e[k], __uint_as_float(uint32_t(sv[k * kSlice128]) << 16), ac);
+    }
+    red[(Wn::kChunks + wave) * 64 + lane] = zc;
+    red[(2 * Wn::kChunks + wave) * 64 + lane] = ac;
+    __syncthreads();
+    // every wave merges the chunks in the same order
+    float Z = red[(Wn::kChunks + first) * 64 + lane], acc = red[(2 * Wn::kChunks + first) * 64 + lane];
+    for (int w = first + 1; w < Wn::kChunks; ++w) {
+      Z = Z + red[(Wn::kChunks + w) * 64 + lane];
+      acc = acc + red[(2 * Wn::kChunks + w) * 64 + lane];
+    }
+    const float R = 1.0f / Z;
+    const float o = acc * R;
+    const float G = R * g;
+    if (present) {
+#pragma unroll
+      for (int k = 0; k < kChunk128; ++k) {
+        const float v = __uint_as_float(uint32_t(sv[k * kSlice128]) << 16);
+        const float a = e[k] * G;
+        const float ds = a * (v - o);
+        dape_r[k] += ds;
+        const uint32_t ab = pack_bf16x2(a, ds);
+        sv[k * kSlice128] = static_cast<uint16_t>(ab & 0xFFFFu);  // dKV over kv
+        ss[k * kSlice128] = static_cast<uint16_t>(ab >> 16);      // dScore over score
+      }
+    }
+    __syncthreads();
+    // store the gradient slices where the window came from (masked rows: none)
+    for (int q = threadIdx.x; q < 2 * Wn::kRows * kParts; q += NT) {
+      const int part = q % kParts, rq = q / kParts;
+      const int tensor = rq / Wn::kRows, k = rq % Wn::kRows;
+      const uint32_t o2 = row128_offset<CO>(k, row.own, CO == 2 && row.has_prev, row_bytes, half_bytes, slice_bytes,
+                                            p.io_bytes);
+      if (o2 == p.io_bytes) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + (tensor * Wn::kRows + k) * kSlice128 + part * 8);
+      __builtin_amdgcn_raw_buffer_store_b128(v, tensor ? rdkv : rdsc, o2 + part * 16u, 0, kAuxStreamStore);
+    }
+    if (row.last) {
+      // the segment's last block owns the never-read slots next to it: its
+      // own rows' first half (coff 2) and the seqlen % 128 tail rows
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const uint32_t tail = row.seg_end - (row.own + kRatio128);
+      const uint32_t nz = (CO == 2 ? kRatio128 : 0) + tail * CO;   // row slices to zero
+      for (uint32_t q = threadIdx.x; q < 2 * nz * kParts; q += NT) {
+        const uint32_t part = q % kParts, rq = q / kParts;
+        const uint32_t tensor = rq / nz, k = rq % nz;
+        uint32_t o2;
+        if (CO == 2 && k < kRatio128) {
+          o2 = (row.own + k) * row_bytes + slice_bytes;
+        } else {
+          const uint32_t kt = k - (CO == 2 ? kRatio128 : 0);
+          o2 = (row.own + kRatio128 + kt / CO) * row_bytes + (kt % CO) * half_bytes + slice_bytes;
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(z, tensor ? rdkv : rdsc, o2 + part * 16u, 0, kAuxStreamStore);
+      }
+    }
+    __syncthreads();  // the next row's staging overwrites stage and red
+  }
+  // dAPE: one partial row per workgroup of a slice (column-block layout)
+  const uint32_t prow = p.partial_rows;
+  const uint32_t nblk = (kRatio128 * W + kPartBlock - 1) / kPartBlock;
+  const rsrc_t rpart = make_rsrc(p.partials, nblk * prow * kPartBlock * 4u);
+#pragma unroll
+  for (int k = 0; k < kChunk128; ++k) {
+    const uint32_t j = (pos0 + k) * W + half * d + col;
+    const uint32_t o2 = ((j / kPartBlock) * prow + wg_in_slice) * kPartBlock + (j % kPartBlock);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dape_r[k]), rpart, o2 * 4u, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Offset scan for packs with more than kMaxLdsSegments segments: one
 // workgroup walks cu in chunks, writes off[0..S] and a validity flag.
 // ---------------------------------------------------------------------------
@@ -1254,6 +1556,42 @@ bool launch_bwd(int ratio, int coff, const BwdParams& p, const LaunchShape& sh, 
   return false;
 }
 
+template <int CO>
+static void launch_fwd128_c(const Fwd128Params& p, uint32_t grid, size_t lds_bytes, hipStream_t st) {
+  const dim3 g(grid), b(Win128<CO>::kThreads);
+  if (p.seg.table == kTableGlobal)
+    hipLaunchKernelGGL((fwd128_kernel<CO, kTableGlobal>), g, b, lds_bytes, st, p);
+  else if (p.seg.table == kTableArgs)
+    hipLaunchKernelGGL((fwd128_kernel<CO, kTableArgs>), g, b, lds_bytes, st, p);
+  else
+    hipLaunchKernelGGL((fwd128_kernel<CO, kTableLds>), g, b, lds_bytes, st, p);
+}
+
+template <int CO>
+static void launch_bwd128_c(const Bwd128Params& p, uint32_t grid, size_t lds_bytes, hipStream_t st) {
+  const dim3 g(grid), b(Win128<CO>::kThreads);
+  if (p.seg.table == kTableGlobal)
+    hipLaunchKernelGGL((bwd128_kernel<CO, kTableGlobal>), g, b, lds_bytes, st, p);
+  else if (p.seg.table == kTableArgs)
+    hipLaunchKernelGGL((bwd128_kernel<CO, kTableArgs>), g, b, lds_bytes, st, p);
+  else
+    hipLaunchKernelGGL((bwd128_kernel<CO, kTableLds>), g, b, lds_bytes, st, p);
+}
+
+bool launch_fwd128(int coff, const Fwd128Params& p, uint32_t grid, size_t lds_bytes, hipStream_t st) {
+  if (coff == 2) launch_fwd128_c<2>(p, grid, lds_bytes, st);
+  else if (coff == 1) launch_fwd128_c<1>(p, grid, lds_bytes, st);
+  else return false;
+  return true;
+}
+
+bool launch_bwd128(int coff, const Bwd128Params& p, uint32_t grid, size_t lds_bytes, hipStream_t st) {
+  if (coff == 2) launch_bwd128_c<2>(p, grid, lds_bytes, st);
+  else if (coff == 1) launch_bwd128_c<1>(p, grid, lds_bytes, st);
+  else return false;
+  return true;
+}
+
 void launch_dape_reduce(const ReduceParams& p, hipStream_t st) {
   const uint32_t grid = (p.cols + kPartBlock - 1) / kPartBlock;
   hipLaunchKernelGGL(dape_reduce_kernel, dim3(grid), dim3(kReduceNT), 0, st, p);
@@ -1266,6 +1604,10 @@ bool launch_seg_scan(int ratio, const SegParams& sp, int32_t* off, int32_t* flag
   }
   if (ratio == 2) {
     hipLaunchKernelGGL(seg_scan_kernel<2>, dim3(1), dim3(kScanNT), 0, st, sp, off, flag);
+    return true;
+  }
+  if (ratio == kRatio128) {
+    hipLaunchKernelGGL(seg_scan_kernel<kRatio128>, dim3(1), dim3(kScanNT), 0, st, sp, off, flag);
     return true;
   }
   return false;

@@ -71,6 +71,43 @@ struct BwdParams {
   uint32_t lds_table_words;
 };
 
+// ratio = 128 (windows of 128 * coff rows): a workgroup owns a slice of
+// kSlice128 columns (one per lane) and walks output rows; the window slice is
+// staged in LDS and each wave takes one chunk of kChunk128 window entries.
+constexpr int kRatio128 = 128;
+constexpr int kSlice128 = 64;
+constexpr int kChunk128 = 64;
+
+struct Fwd128Params {
+  SegParams seg;
+  const uint16_t* kv;
+  const uint16_t* score;
+  const float* ape;
+  uint16_t* out;
+  uint32_t io_bytes;
+  uint32_t head_dim;
+  uint32_t nslices;       // head_dim / kSlice128
+  uint32_t lds_table_words;
+};
+
+struct Bwd128Params {
+  SegParams seg;
+  const uint16_t* kv;
+  const uint16_t* score;
+  const float* ape;
+  const uint16_t* dout;
+  uint16_t* dkv;
+  uint16_t* dscore;
+  float* partials;        // column blocks [ceil(128*W/kPartBlock)][partial_rows][kPartBlock]
+  int32_t* ws_flag;
+  uint32_t io_bytes;
+  uint32_t head_dim;
+  uint32_t nslices;
+  uint32_t main_wgs;      // workgroups [0, main_wgs) compute windows, the rest zero-fill
+  uint32_t partial_rows;  // main_wgs / nslices
+  uint32_t lds_table_words;
+};
+
 struct ReduceParams {
   const float* partials;
   float* dape;
@@ -93,5 +130,7 @@ bool launch_fwd(int ratio, int coff, const FwdParams& p, const LaunchShape& sh, 
 bool launch_bwd(int ratio, int coff, const BwdParams& p, const LaunchShape& sh, hipStream_t st);
 void launch_dape_reduce(const ReduceParams& p, hipStream_t st);
 bool launch_seg_scan(int ratio, const SegParams& sp, int32_t* off, int32_t* flag, hipStream_t st);
+bool launch_fwd128(int coff, const Fwd128Params& p, uint32_t grid, size_t lds_bytes, hipStream_t st);
+bool launch_bwd128(int coff, const Bwd128Params& p, uint32_t grid, size_t lds_bytes, hipStream_t st);
 
 }  // namespace csa

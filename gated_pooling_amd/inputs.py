@@ -87,6 +87,14 @@ def _build_workloads():
     for c in (1, 2):
         add(f"ragged_d128_r4_c{c}", _cu_from_lengths(ragged_lengths(4)), 32768, 4, c, 128,
             "uniform [1,4096] lengths + 1, ratio-1 and 0-token segments, 32768-row buffer")
+    # ratio 128 (windows of 128 * coff rows): the pages time 8k-131k-token
+    # packs at coff {1, 2} x head_dim {128, 512}
+    for c in (1, 2):
+        for d in (128, 512):
+            add(f"1x65536_d{d}_r128_c{c}", _uniform_pack(1, 65536), 65536, 128, c, d)
+    add("8x8192_d512_r128_c2", _uniform_pack(8, 8192), 65536, 128, 2, 512)
+    add("ragged_d128_r128_c2", _cu_from_lengths(ragged_lengths(128)), 32768, 128, 2, 128,
+        "uniform [1,4096] lengths + 1, ratio-1 and 0-token segments, 32768-row buffer")
     return w
 
 

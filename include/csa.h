@@ -33,6 +33,10 @@
  *   (window order);  R = 1/Z (correctly rounded);  acc = fma chain of e*v
  *   from 0;  o = acc*R;  out = bf16_rne(o);  backward: G = R*f32(dout),
  *   a = e*G, dkv = bf16_rne(a), ds = a*(v - o), dscore = bf16_rne(ds).
+ *   Windows longer than 64 entries (ratio 128) sum Z and acc per chunk of 64
+ *   consecutive entries as above and then add the chunk sums in chunk order
+ *   ([PR5984: ratio=128 commit]: per-chunk partials merged in one fixed
+ *   order).
  *   EXP(y) = ldexp(P6(r), k) with y clamped to >= -104, k = rint(y*log2 e),
  *   r = y - k*ln2 in two fma steps, P6 the degree-6 Taylor polynomial of
  *   e^r (coefficients fp32(1/n!)); IEEE subnormals are kept.
@@ -83,8 +87,9 @@ typedef enum csa_status {
     /* a null or misaligned pointer, a negative size, inconsistent sizes
      * (e.g. total_comp * ratio > total_tokens), an undersized output */
     CSA_STATUS_INVALID_VALUE = 1,
-    /* outside the validated envelope: ratio not in {2, 4}, coff not in
-     * {1, 2}, head_dim not in [1, 1024], or one of
+    /* outside the validated envelope: ratio not in {2, 4, 128}, coff not in
+     * {1, 2}, head_dim not in [1, 1024] (a multiple of 64 at ratio 128),
+     * or one of
      * (total_tokens+1)*coff*head_dim, total_comp*head_dim,
      * ratio*coff*head_dim not below 2^31 (each checked on its own) */
     CSA_STATUS_NOT_SUPPORTED = 2,

@@ -46,6 +46,14 @@
  *             Z   = ((e_0 + e_1) + e_2) + ...              (window order)
  *             R   = 1 / Z                                  (correctly rounded)
  *             acc = fma(e_{K-1}, v_{K-1}, ... fma(e_0, v_0, 0))
+ *           Windows longer than SUM_CHUNK = 64 entries (ratio 128) sum in
+ *           chunks of 64 consecutive entries instead: each chunk's Z and acc
+ *           as above over its own entries, then the chunk sums added in
+ *           chunk order, Z = ((Z_0 + Z_1) + Z_2) + ..., acc likewise
+ *           ([PR5984: ratio=128 commit] merges per-chunk partials in one
+ *           fixed order; the window max is taken over the whole window
+ *           first, so no rescaling is needed).  Windows of at most 64
+ *           entries are one chunk: the rule above.
  *             o   = acc * R,  out = bf16_rne(o)
  *             G   = R * f32(dOut),  a_k = e_k * G
  *             dKV_k = bf16_rne(a_k),  ds_k = a_k * (v_k - o),
@@ -248,6 +256,9 @@ static void free_blocks(blocks_t* bl)
 /* fp32 oracle (fixed evaluation order, see header)                        */
 /* ---------------------------------------------------------------------- */
 
+/* Window entries per summation chunk (see the header). */
+#define SUM_CHUNK 64
+
 /* Shared body of the fp32 forward and backward: one (block, column) window.
  * Fills e[], v[], returns R and o. */
 static void window_f32(const uint16_t* kv, const uint16_t* score,
@@ -264,11 +275,17 @@ static void window_f32(const uint16_t* kv, const uint16_t* score,
     float m = x[0];
     for (int k = 1; k < K; ++k) m = fmaxf(m, x[k]);
     for (int k = 0; k < K; ++k) e[k] = oracle_exp_f32(x[k] - m);
-    float Z = e[0];
-    for (int k = 1; k < K; ++k) Z = Z + e[k];
+    float Z = 0.0f, acc = 0.0f;
+    for (int c0 = 0; c0 < K; c0 += SUM_CHUNK) {
+        const int c1 = (c0 + SUM_CHUNK < K) ? c0 + SUM_CHUNK : K;
+        float zc = e[c0];
+        for (int k = c0 + 1; k < c1; ++k) zc = zc + e[k];
+        float ac = 0.0f;
+        for (int k = c0; k < c1; ++k) ac = fmaf(e[k], v[k], ac);
+        Z = (c0 == 0) ? zc : Z + zc;
+        acc = (c0 == 0) ? ac : acc + ac;
+    }
     float R = 1.0f / Z;
-    float acc = 0.0f;
-    for (int k = 0; k < K; ++k) acc = fmaf(e[k], v[k], acc);
     *R_out = R;
     *o_out = acc * R;
 }

@@ -67,6 +67,8 @@ def test_workloads_are_supported(name):
 @pytest.mark.parametrize("args,exc", [
     ((3, 2, 16, 2, 64, 15), G.CsaNotSupported),       # ratio 3
     ((8, 2, 16, 2, 64, 8), G.CsaNotSupported),        # ratio 8
+    ((128, 2, 96, 2, 512, 1), G.CsaNotSupported),     # ratio 128 needs head_dim % 64 == 0
+    ((64, 2, 128, 2, 512, 1), G.CsaNotSupported),     # ratio 64
     ((4, 0, 16, 2, 64, 15), G.CsaNotSupported),       # coff 0
     ((4, 3, 16, 2, 64, 15), G.CsaNotSupported),       # coff 3
     ((2, 0, 16, 2, 64, 15), G.CsaNotSupported),       # coff 0 at ratio 2

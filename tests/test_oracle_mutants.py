@@ -31,7 +31,10 @@ MUTANTS = [
      "+ 0.0f * ape[(int64_t)pos[k] * W + col];\n        v[k] = oracle_f32_from_bf16"),
     ("ape_dropped_f64", "x[k] = score[rows[k] * W + col] + ape[(int64_t)pos[k] * W + col];",
      "x[k] = score[rows[k] * W + col];"),
-    ("sum_skips_an_entry", "for (int k = 1; k < K; ++k) Z = Z + e[k];", "for (int k = 2; k < K; ++k) Z = Z + e[k];"),
+    ("sum_skips_an_entry", "for (int k = c0 + 1; k < c1; ++k) zc = zc + e[k];",
+     "for (int k = c0 + 2; k < c1; ++k) zc = zc + e[k];"),
+    ("chunk_sum_drops_earlier_chunks", "Z = (c0 == 0) ? zc : Z + zc;", "Z = zc;"),
+    ("chunk_acc_drops_earlier_chunks", "acc = (c0 == 0) ? ac : acc + ac;", "acc = ac;"),
     ("wrong_normaliser", "float R = 1.0f / Z;", "float R = 1.0f / (Z + e[0]);"),
     ("f64_unnormalised", "p[k] = p[k] / Z;", "p[k] = p[k] / (Z + 1.0);"),
     ("bwd_sign_f32", "float dsk = a * (v[k] - o);", "float dsk = a * (o - v[k]);"),

@@ -136,7 +136,7 @@ def test_stage_split_equals_full_backward(dev):
 
 
 @pytest.mark.parametrize("name", ["3x8192_d512_r4_c2", "ragged_d128_r4_c1", "ragged_d128_r4_c2",
-                                  "1x8192_d128_r2_c2"])
+                                  "1x8192_d128_r2_c2", "ragged_d128_r128_c2"])
 def test_repeat_runs_bit_identical(dev, name):
     wl = inputs.WORKLOADS[name]
     cu, T, r, c, d = list(wl.cu_seqlens), wl.total_tokens, wl.ratio, wl.coff, wl.head_dim
@@ -272,6 +272,38 @@ def test_non_power_of_two_head_dims(dev, case):
     for host in (True, False):
         got = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N, host=host)
         check_against_oracle(cu, T, r, c, d, kv, sc, ape, dout, got)
+
+
+def _r128_cases():
+    rng = np.random.default_rng(128)
+    cases = []
+    for i in range(10):
+        nseg = int(rng.integers(1, 6))
+        lengths = rng.integers(0, 700, size=nseg).tolist()
+        lengths[int(rng.integers(0, nseg))] = int(rng.integers(1, 128))  # shorter than ratio
+        T = int(sum(lengths)) + int(rng.integers(1, 300))                # padding rows
+        c = int(rng.choice([1, 2]))
+        d = int(rng.choice([64, 128, 192, 512]))
+        cases.append((lengths, T, c, d, 900 + i, bool(i % 2)))
+    lengths = rng.integers(0, 400, size=60).tolist()                     # 60 segments: LDS table
+    cases.append((lengths, int(sum(lengths)) + 7, 2, 64, 950, False))
+    lengths = rng.integers(0, 260, size=2300).tolist()                   # workspace table
+    cases.append((lengths, int(sum(lengths)) + 7, 1, 64, 951, False))
+    return cases
+
+
+@pytest.mark.parametrize("case", _r128_cases(), ids=lambda c: f"S{len(c[0])}_c{c[2]}_d{c[3]}_s{c[4]}")
+def test_ratio128_packs(dev, case):
+    """ratio 128: windows of 128 * coff rows staged through LDS, chunked
+    sums; multi-block segments, tails, segments shorter than 128, padding,
+    kernel-argument / LDS / workspace segment tables."""
+    lengths, T, c, d, seed, host = case
+    wl = inputs.custom("r128", lengths, T, 128, c, d, seed=seed)
+    cu = list(wl.cu_seqlens)
+    N = G.csa_compressor_total_comp(cu, 128)
+    kv, sc, ape, dout = inputs.make_tensors(wl, N)
+    got = run_gpu(dev, cu, T, 128, c, d, kv, sc, ape, dout, N, host=host)
+    check_against_oracle(cu, T, 128, c, d, kv, sc, ape, dout, got)
 
 
 def test_extreme_scores_and_subnormals(dev):
