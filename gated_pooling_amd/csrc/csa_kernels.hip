@@ -1137,19 +1137,30 @@ __device__ __forceinline__ Row128 row128(uint32_t n, int& s_hint, const UTable<T
 }
 
 // Stage the window's score and kv slices in LDS: stage[tensor][k][64] bf16.
+// Every load of a thread is issued before the first LDS write, so the whole
+// window is one round trip from memory.
 template <int CO>
 __device__ __forceinline__ void stage_window128(uint16_t* stage, rsrc_t rsc, rsrc_t rkv, const Row128& row,
                                                 uint32_t row_bytes, uint32_t half_bytes, uint32_t slice_bytes,
                                                 uint32_t oob) {
   using Wn = Win128<CO>;
   constexpr int kParts = kSlice128 * 2 / 16;  // 16-byte parts of a row slice
-  for (int q = threadIdx.x; q < 2 * Wn::kRows * kParts; q += Wn::kThreads) {
+  constexpr int kIters = 2 * Wn::kRows * kParts / Wn::kThreads;
+  static_assert(2 * Wn::kRows * kParts % Wn::kThreads == 0, "whole iterations");
+  u32x4 v[kIters];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int q = threadIdx.x + it * Wn::kThreads;
     const int part = q % kParts, rq = q / kParts;
     const int tensor = rq / Wn::kRows, k = rq % Wn::kRows;
     const uint32_t o = row128_offset<CO>(k, row.own, CO == 2 && row.has_prev, row_bytes, half_bytes, slice_bytes, oob);
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(tensor ? rkv : rsc, o == oob ? oob : o + part * 16u, 0,
-                                                          kAuxStream);
-    *reinterpret_cast<u32x4*>(stage + (tensor * Wn::kRows + k) * kSlice128 + part * 8) = v;
+    v[it] = __builtin_amdgcn_raw_buffer_load_b128(tensor ? rkv : rsc, o == oob ? oob : o + part * 16u, 0, kAuxStream);
+  }
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int q = threadIdx.x + it * Wn::kThreads;
+    const int part = q % kParts, rq = q / kParts;
+    *reinterpret_cast<u32x4*>(stage + rq * kSlice128 + part * 8) = v[it];
   }
 }
 
