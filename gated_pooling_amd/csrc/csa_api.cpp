@@ -70,8 +70,8 @@ struct Tuning {
   int uniform = 1;        // wave-uniform row path where a row has >= 64 chunks
   int fwd_prefetch = 2;   // windows in flight per lane (uniform path)
   int bwd_prefetch = 3;
-  int r128_fwd_wgs = 512; // ratio 128 grid caps (workgroups)
-  int r128_bwd_wgs = 256;
+  int r128_fwd_wgs = 0;   // ratio 128 grid caps (workgroups); 0: by coff
+  int r128_bwd_wgs = 0;
 };
 
 int env_int(const char* name, int dflt, const int* allowed, int n_allowed, int lo, int hi) {
@@ -205,31 +205,36 @@ Plan make_plan_r128(const Problem& p) {
   const int64_t W = int64_t{p.coff} * p.head_dim;
   pl.global_table = p.S > csa::kMaxLdsSegments;
   pl.off_bytes = pl.global_table ? align_up(uint64_t(p.S + 1) * 4, 256) : 0;
-  const int NT = p.coff * 128;                       // one wave per 64-entry chunk
-  const int chunks = p.coff * 2;
-  const uint64_t stage_bytes = 2ull * p.coff * csa::kRatio128 * csa::kSlice128 * 2;
-  const uint64_t red_bytes = 3ull * chunks * 64 * 4;
-  // the staged window follows the table in LDS and is accessed 16 bytes at a
-  // time: keep it 16-byte aligned
+  const int rows = p.coff * csa::kRatio128;           // window rows
+  const int chunks = rows / csa::kChunk128;
+  const int NT = 2 * chunks * 64;                      // two waves per 64-entry chunk
+  // two exchange sets: wave maxima, part-0 chains, chunk sums
+  const uint64_t red_bytes = 2ull * (2 * chunks * 64 + 4 * chunks * 64) * 4;
+  const uint64_t ape_bytes = uint64_t(rows) * csa::kSlice128 * 4;   // backward: APE slice
   const uint32_t table_words =
       pl.global_table ? 0 : static_cast<uint32_t>(align_up(2 * (NT / 64) + 2 * uint64_t(p.S + 1), 4));
   pl.nslices = static_cast<uint32_t>(p.head_dim / csa::kSlice128);
-  const int64_t rows = p.N > 0 ? p.N : 1;
+  const int64_t out_rows = p.N > 0 ? p.N : 1;
   {
-    int64_t per = tu.r128_fwd_wgs / pl.nslices;
+    // measured on 65536-token packs: the forward keeps 4 waves per SIMD at
+    // either coff, the backward 2 (one 512-thread workgroup per CU at coff 2,
+    // two 256-thread workgroups at coff 1)
+    const int cap = tu.r128_fwd_wgs ? tu.r128_fwd_wgs : (p.coff == 2 ? 512 : 1024);
+    int64_t per = cap / pl.nslices;
     if (per < 1) per = 1;
-    if (per > rows) per = rows;
+    if (per > out_rows) per = out_rows;
     pl.fwd.grid = static_cast<uint32_t>(per * pl.nslices);
     pl.fwd.threads = NT;
     pl.fwd.cols = 1;
     pl.fwd_lds_table_words = table_words;
-    pl.fwd.lds_bytes = table_words * 4ull + stage_bytes + red_bytes;
+    pl.fwd.lds_bytes = table_words * 4ull + red_bytes;
     pl.ws_fwd = pl.global_table ? kHeaderBytes + pl.off_bytes : 0;
   }
   {
-    int64_t per = tu.r128_bwd_wgs / pl.nslices;
+    const int cap = tu.r128_bwd_wgs ? tu.r128_bwd_wgs : (p.coff == 2 ? 256 : 512);
+    int64_t per = cap / pl.nslices;
     if (per < 1) per = 1;
-    if (per > rows) per = rows;
+    if (per > out_rows) per = out_rows;
     const int64_t main = per * pl.nslices;
     const int64_t spare_rows = p.T - p.N * p.ratio;
     int64_t zero = 0;
@@ -245,7 +250,7 @@ Plan make_plan_r128(const Problem& p) {
     pl.bwd_main_wgs = static_cast<uint32_t>(main);
     pl.partial_rows = static_cast<uint32_t>(per);
     pl.lds_table_words = table_words;
-    pl.bwd.lds_bytes = table_words * 4ull + stage_bytes + red_bytes;
+    pl.bwd.lds_bytes = table_words * 4ull + ape_bytes + red_bytes;
     pl.partial_offset = kHeaderBytes + pl.off_bytes;
     const uint64_t nblk = (uint64_t(p.ratio) * W + csa::kPartBlock - 1) / csa::kPartBlock;
     pl.ws_bwd = pl.partial_offset + align_up(nblk * pl.partial_rows * csa::kPartBlock * 4, 256);

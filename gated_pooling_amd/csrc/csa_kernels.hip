@@ -1077,42 +1077,38 @@ __global__ __launch_bounds__(kReduceNT) void dape_reduce_kernel(ReduceParams p) 
 
 // ---------------------------------------------------------------------------
 // ratio = 128 [PR5984: ratio=128 commit]: a window holds 128 * coff rows per
-// column, too many for registers.  A workgroup owns a slice of kSlice128
-// columns (lane = column) and walks output rows; per row:
-//   1. the window's row slices (score and kv, 128 bytes each) are staged in
-//      LDS with 16-byte loads;
-//   2. wave w takes window entries [64w, 64w + 64) (one summation chunk):
-//      x_k = score + ape, the chunk max, exchanged through LDS -> window max m;
-//   3. e_k = EXP(x_k - m), the chunk's Z (from its first e) and acc (fma chain
-//      from 0), merged in chunk order through LDS: exactly the chunked fp32
+// column, too many for one lane's registers.  A workgroup owns a slice of
+// kSlice128 columns (lane = column) and walks output rows.  Each 64-entry
+// summation chunk of the window is held by two waves, 32 entries each
+// (`part` 0 and 1), so a lane keeps 32 window entries and every 16-bit load
+// and store of a wave covers one 128-byte line of one row.  Per row:
+//   1. each wave loads its 32 score and kv entries straight into registers;
+//      x = score + ape, the wave's max, exchanged through LDS -> window max m;
+//   2. e = EXP(x - m); part 0 starts the chunk's Z (from its first e) and acc
+//      (fma chain from 0), part 1 continues both chains from part 0's values
+//      (handed over through LDS), so every chunk is summed in entry order;
+//      the chunk sums are then added in chunk order: exactly the chunked fp32
 //      order of windows above 64 entries (the first block at coff 2 has only
 //      the own half: chunks 2 and 3);
-//   backward 4. a_k = e_k * R * g, ds_k = a_k (v_k - o), bf16 results written
-//      over the staged inputs in LDS, then stored with 16-byte stores; dAPE
-//      sums stay in registers (a wave always holds the same 64 positions of
-//      its slice) and leave as one partial row per workgroup.
-// head_dim is a multiple of kSlice128, so every row slice is whole.
+//   backward 3. a = e * R * g, ds = a (v - o), bf16 results stored to the
+//      slots the window came from; dAPE sums stay in registers (a wave always
+//      holds the same 32 positions of its slice) and leave as one partial row
+//      per workgroup.
+// LDS holds only the exchange buffers (two sets, alternating between rows)
+// and, in the backward, the workgroup's APE slice.  head_dim is a multiple of
+// kSlice128, so every row slice is whole.
 // ---------------------------------------------------------------------------
 template <int CO>
 struct Win128 {
   static constexpr int kRows = CO * kRatio128;        // window rows
-  static constexpr int kChunks = kRows / kChunk128;   // summation chunks (= waves)
-  static constexpr int kThreads = kChunks * 64;
-  static constexpr int kStageBytes = 2 * kRows * kSlice128 * 2;  // score, kv as bf16
+  static constexpr int kChunks = kRows / kChunk128;   // summation chunks
+  static constexpr int kPart = kChunk128 / 2;         // entries per wave
+  static constexpr int kWaves = 2 * kChunks;
+  static constexpr int kThreads = kWaves * 64;
+  // one exchange set: wave maxima [kWaves][64], part-0 chains [2][kChunks][64],
+  // chunk sums [2][kChunks][64]
+  static constexpr int kRedFloats = kWaves * 64 + 4 * kChunks * 64;
 };
-
-// Byte offset in kv/score of window row k's slice, or `oob` when the row is
-// masked (the previous half of a segment's first block).
-template <int CO>
-__device__ __forceinline__ uint32_t row128_offset(int k, uint32_t own, bool has_prev, uint32_t row_bytes,
-                                                  uint32_t half_bytes, uint32_t slice_bytes, uint32_t oob) {
-  if constexpr (CO == 2) {
-    if (k < kRatio128) return has_prev ? (own - kRatio128 + k) * row_bytes + slice_bytes : oob;
-    return (own + k - kRatio128) * row_bytes + half_bytes + slice_bytes;
-  } else {
-    return (own + k) * row_bytes + slice_bytes;
-  }
-}
 
 // Row of output row n (uniform): segment lookup on the scalar unit.
 struct Row128 {
@@ -1136,117 +1132,145 @@ __device__ __forceinline__ Row128 row128(uint32_t n, int& s_hint, const UTable<T
   return r;
 }
 
-// Stage the window's score and kv slices in LDS: stage[tensor][k][64] bf16.
-// Every load of a thread is issued before the first LDS write, so the whole
-// window is one round trip from memory.
+// A wave's place in the window: chunk, part, half and first block position.
 template <int CO>
-__device__ __forceinline__ void stage_window128(uint16_t* stage, rsrc_t rsc, rsrc_t rkv, const Row128& row,
-                                                uint32_t row_bytes, uint32_t half_bytes, uint32_t slice_bytes,
-                                                uint32_t oob) {
-  using Wn = Win128<CO>;
-  constexpr int kParts = kSlice128 * 2 / 16;  // 16-byte parts of a row slice
-  constexpr int kIters = 2 * Wn::kRows * kParts / Wn::kThreads;
-  static_assert(2 * Wn::kRows * kParts % Wn::kThreads == 0, "whole iterations");
-  u32x4 v[kIters];
-#pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int q = threadIdx.x + it * Wn::kThreads;
-    const int part = q % kParts, rq = q / kParts;
-    const int tensor = rq / Wn::kRows, k = rq % Wn::kRows;
-    const uint32_t o = row128_offset<CO>(k, row.own, CO == 2 && row.has_prev, row_bytes, half_bytes, slice_bytes, oob);
-    v[it] = __builtin_amdgcn_raw_buffer_load_b128(tensor ? rkv : rsc, o == oob ? oob : o + part * 16u, 0, kAuxStream);
+struct Wave128 {
+  int chunk, part, half;
+  uint32_t pos0;        // block position of the wave's first entry
+  __device__ __forceinline__ explicit Wave128(int wave) {
+    chunk = wave >> 1;
+    part = wave & 1;
+    half = (CO == 2) ? (chunk >> 1) : 0;
+    pos0 = (chunk & 1) * kChunk128 + part * Win128<CO>::kPart;
   }
+  // byte offset of the wave's first entry's row slice in kv/score (uniform)
+  __device__ __forceinline__ uint32_t base(const Row128& row, uint32_t row_bytes, uint32_t half_bytes,
+                                           uint32_t slice_bytes) const {
+    const uint32_t r0 = (CO == 2 && half == 0) ? row.own - kRatio128 + pos0 : row.own + pos0;
+    return r0 * row_bytes + ((CO == 2 && half == 1) ? half_bytes : 0u) + slice_bytes;
+  }
+  // the previous-half waves of a segment's first block have no entries
+  __device__ __forceinline__ bool present(const Row128& row) const { return !(CO == 2 && half == 0 && !row.has_prev); }
+};
+
+// Window max and chunk sums through one exchange set.  x holds the wave's
+// logits on entry and its e = EXP(x - m) on return; Z/acc are the window's.
+// Returns false (and leaves Z/acc unset) for lanes of absent waves.
+template <int CO>
+__device__ __forceinline__ void softmax128(float (&x)[Win128<CO>::kPart], const uint32_t (&v)[Win128<CO>::kPart],
+                                           bool present, bool has_prev, int wave, int lane, const Wave128<CO>& wv,
+                                           float* red, float& Z, float& acc) {
+  using Wn = Win128<CO>;
+  constexpr int K = Wn::kPart;
+  float* rm = red;                                  // [kWaves][64]
+  float* rz0 = red + Wn::kWaves * 64;               // [kChunks][64] part-0 Z
+  float* ra0 = rz0 + Wn::kChunks * 64;              // [kChunks][64] part-0 acc
+  float* rz = ra0 + Wn::kChunks * 64;               // [kChunks][64] chunk Z
+  float* ra = rz + Wn::kChunks * 64;                // [kChunks][64] chunk acc
+  const int first_w = (CO == 2 && !has_prev) ? Wn::kWaves / 2 : 0;
+  if (present) {
+    float m = x[0];
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int q = threadIdx.x + it * Wn::kThreads;
-    const int part = q % kParts, rq = q / kParts;
-    *reinterpret_cast<u32x4*>(stage + rq * kSlice128 + part * 8) = v[it];
+    for (int k = 1; k < K; ++k) m = fmaxf(m, x[k]);
+    rm[wave * 64 + lane] = m;
+  }
+  __syncthreads();
+  float m = rm[first_w * 64 + lane];
+  for (int w = first_w + 1; w < Wn::kWaves; ++w) m = fmaxf(m, rm[w * 64 + lane]);
+#pragma unroll
+  for (int k = 0; k < K; ++k) x[k] = csa_exp(x[k] - m);
+  if (present && wv.part == 0) {
+    float zc = x[0], ac = 0.0f;
+#pragma unroll
+    for (int k = 1; k < K; ++k) zc = zc + x[k];
+#pragma unroll
+    for (int k = 0; k < K; ++k) ac = __builtin_fmaf(x[k], __uint_as_float(v[k] << 16), ac);
+    rz0[wv.chunk * 64 + lane] = zc;
+    ra0[wv.chunk * 64 + lane] = ac;
+  }
+  __syncthreads();
+  if (present && wv.part == 1) {
+    float zc = rz0[wv.chunk * 64 + lane], ac = ra0[wv.chunk * 64 + lane];
+#pragma unroll
+    for (int k = 0; k < K; ++k) zc = zc + x[k];
+#pragma unroll
+    for (int k = 0; k < K; ++k) ac = __builtin_fmaf(x[k], __uint_as_float(v[k] << 16), ac);
+    rz[wv.chunk * 64 + lane] = zc;
+    ra[wv.chunk * 64 + lane] = ac;
+  }
+  __syncthreads();
+  const int first_c = first_w / 2;
+  Z = rz[first_c * 64 + lane];
+  acc = ra[first_c * 64 + lane];
+  for (int c = first_c + 1; c < Wn::kChunks; ++c) {
+    Z = Z + rz[c * 64 + lane];
+    acc = acc + ra[c * 64 + lane];
   }
 }
 
 template <int CO, int TBL>
 __global__ __launch_bounds__(Win128<CO>::kThreads) void fwd128_kernel(Fwd128Params p) {
   using Wn = Win128<CO>;
-  constexpr int NT = Wn::kThreads;
+  constexpr int NT = Wn::kThreads, K = Wn::kPart;
   extern __shared__ int32_t lds[];
   SegTable tab{nullptr, nullptr};
   if constexpr (TBL != kTableArgs) {
     if (!load_segment_table<kRatio128, NT, TBL>(p.seg, lds, tab)) return;
   }
-  uint16_t* stage = reinterpret_cast<uint16_t*>(lds + p.lds_table_words);
-  float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(stage) + Wn::kStageBytes);  // [3][kChunks][64]
+  float* red = reinterpret_cast<float*>(lds + p.lds_table_words);  // two exchange sets
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const Wave128<CO> wv(wave);
   const uint32_t d = p.head_dim, W = CO * d, N = static_cast<uint32_t>(p.seg.N);
   const uint32_t nslices = p.nslices, slice = blockIdx.x % nslices, per_slice = gridDim.x / nslices;
   const uint32_t col = slice * kSlice128 + lane;
-  const uint32_t half = (CO == 2) ? (wave >> 1) : 0;   // the chunk's half of the row
-  const uint32_t pos0 = (wave & 1) * kChunk128;        // its first position in the block
   const rsrc_t rkv = make_rsrc(p.kv, p.io_bytes);
   const rsrc_t rsc = make_rsrc(p.score, p.io_bytes);
   const rsrc_t rape = make_rsrc(p.ape, kRatio128 * W * 4u);
   const rsrc_t rout = make_rsrc(p.out, N * d * 2u);
-  float ape_r[kChunk128];
+  float ape_r[K];
 #pragma unroll
-  for (int k = 0; k < kChunk128; ++k)
-    ape_r[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rape, ((pos0 + k) * W + half * d + col) * 4u, 0, 0));
+  for (int k = 0; k < K; ++k)
+    ape_r[k] = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rape, ((wv.pos0 + k) * W + wv.half * d + col) * 4u, 0, 0));
 
   const UTable<TBL> t{p.seg, tab.cu, tab.off};
   int s_hint = 0;
   const uint32_t row_bytes = W * 2u, half_bytes = d * 2u, slice_bytes = slice * kSlice128 * 2u;
-  for (uint32_t n = __builtin_amdgcn_readfirstlane(blockIdx.x / nslices); n < N; n += per_slice) {
+  const uint32_t lane_off = lane * 2u;
+  uint32_t set = 0;
+  for (uint32_t n = __builtin_amdgcn_readfirstlane(blockIdx.x / nslices); n < N; n += per_slice, set ^= 1u) {
     const Row128 row = row128<TBL>(n, s_hint, t, p.seg.S);
-    stage_window128<CO>(stage, rsc, rkv, row, row_bytes, half_bytes, slice_bytes, p.io_bytes);
-    __syncthreads();
-    const bool present = !(CO == 2 && wave < 2 && !row.has_prev);
-    const uint16_t* ss = stage + (wave * kChunk128) * kSlice128 + lane;
-    const uint16_t* sv = stage + (Wn::kRows + wave * kChunk128) * kSlice128 + lane;
-    float x[kChunk128];
-    float m = 0.0f;
+    const bool present = wv.present(row);
+    float x[K];
+    uint32_t v[K];
     if (present) {
+      const uint32_t b = wv.base(row, row_bytes, half_bytes, slice_bytes);
+      uint32_t sc[K];
 #pragma unroll
-      for (int k = 0; k < kChunk128; ++k) x[k] = __uint_as_float(uint32_t(ss[k * kSlice128]) << 16) + ape_r[k];
-      m = x[0];
+      for (int k = 0; k < K; ++k) sc[k] = __builtin_amdgcn_raw_buffer_load_b16(rsc, lane_off, b + k * row_bytes, kAuxStream);
 #pragma unroll
-      for (int k = 1; k < kChunk128; ++k) m = fmaxf(m, x[k]);
+      for (int k = 0; k < K; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b16(rkv, lane_off, b + k * row_bytes, kAuxStream);
+#pragma unroll
+      for (int k = 0; k < K; ++k) x[k] = __uint_as_float(sc[k] << 16) + ape_r[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < K; ++k) { x[k] = 0.0f; v[k] = 0u; }
     }
-    const int first = (CO == 2 && !row.has_prev) ? 2 : 0;
-    red[wave * 64 + lane] = m;
-    __syncthreads();
-    m = red[first * 64 + lane];
-    for (int w = first + 1; w < Wn::kChunks; ++w) m = fmaxf(m, red[w * 64 + lane]);
-    float zc = 0.0f, ac = 0.0f;
-    if (present) {
-      float e[kChunk128];
-#pragma unroll
-      for (int k = 0; k < kChunk128; ++k) e[k] = csa_exp(x[k] - m);
-      zc = e[0];
-#pragma unroll
-      for (int k = 1; k < kChunk128; ++k) zc = zc + e[k];
-#pragma unroll
-      for (int k = 0; k < kChunk128; ++k) ac = __builtin_fmaf(e[k], __uint_as_float(uint32_t(sv[k * kSlice128]) << 16), ac);
-    }
-    red[(Wn::kChunks + wave) * 64 + lane] = zc;
-    red[(2 * Wn::kChunks + wave) * 64 + lane] = ac;
-    __syncthreads();
+    float Z, acc;
+    softmax128<CO>(x, v, present, row.has_prev, wave, lane, wv, red + set * Wn::kRedFloats, Z, acc);
     if (wave == 0) {
-      float Z = red[(Wn::kChunks + first) * 64 + lane], acc = red[(2 * Wn::kChunks + first) * 64 + lane];
-      for (int w = first + 1; w < Wn::kChunks; ++w) {
-        Z = Z + red[(Wn::kChunks + w) * 64 + lane];
-        acc = acc + red[(2 * Wn::kChunks + w) * 64 + lane];
-      }
       const float o = acc * (1.0f / Z);
       const Pack<1> ob{{pack_bf16x2(o, 0.0f)}};
       store_pack<1>(rout, (n * d + col) * 2u, ob);
     }
-    __syncthreads();  // the next row's staging overwrites stage and red
   }
 }
 
 template <int CO, int TBL>
 __global__ __launch_bounds__(Win128<CO>::kThreads) void bwd128_kernel(Bwd128Params p) {
   using Wn = Win128<CO>;
-  constexpr int NT = Wn::kThreads;
+  constexpr int NT = Wn::kThreads, K = Wn::kPart;
   extern __shared__ int32_t lds[];
   SegTable tab{nullptr, nullptr};
   bool valid = true;
@@ -1261,99 +1285,76 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void bwd128_kernel(Bwd128Para
     zero_sweep<kRatio128, CO, NT>(p, tab);
     return;
   }
-  uint16_t* stage = reinterpret_cast<uint16_t*>(lds + p.lds_table_words);
-  float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(stage) + Wn::kStageBytes);
+  // LDS: [table][APE slice: kRows x 64 fp32][two exchange sets]
+  float* ape_s = reinterpret_cast<float*>(lds + p.lds_table_words);
+  float* red = ape_s + Wn::kRows * kSlice128;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const Wave128<CO> wv(wave);
   const uint32_t d = p.head_dim, W = CO * d, N = static_cast<uint32_t>(p.seg.N);
   const uint32_t nslices = p.nslices, slice = blockIdx.x % nslices, per_slice = p.main_wgs / nslices;
   const uint32_t wg_in_slice = blockIdx.x / nslices;
   const uint32_t col = slice * kSlice128 + lane;
-  const uint32_t half = (CO == 2) ? (wave >> 1) : 0;
-  const uint32_t pos0 = (wave & 1) * kChunk128;
   const rsrc_t rkv = make_rsrc(p.kv, p.io_bytes);
   const rsrc_t rsc = make_rsrc(p.score, p.io_bytes);
   const rsrc_t rdkv = make_rsrc(p.dkv, p.io_bytes);
   const rsrc_t rdsc = make_rsrc(p.dscore, p.io_bytes);
   const rsrc_t rape = make_rsrc(p.ape, kRatio128 * W * 4u);
   const rsrc_t rdo = make_rsrc(p.dout, N * d * 2u);
-  float ape_r[kChunk128], dape_r[kChunk128];
-#pragma unroll
-  for (int k = 0; k < kChunk128; ++k) {
-    ape_r[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rape, ((pos0 + k) * W + half * d + col) * 4u, 0, 0));
-    dape_r[k] = 0.0f;
+  // APE slice: entry (half, position) of the window at ape_s[(half * 128 + pos) * 64 + lane]
+  for (int q = threadIdx.x; q < Wn::kRows * kSlice128; q += NT) {
+    const uint32_t hp = q / kSlice128, c = q % kSlice128, h = hp / kRatio128, pos = hp % kRatio128;
+    ape_s[q] = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rape, (pos * W + h * d + slice * kSlice128 + c) * 4u, 0, 0));
   }
+  __syncthreads();
+  const float* ape_w = ape_s + (wv.half * kRatio128 + wv.pos0) * kSlice128 + lane;
+  float dape_r[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) dape_r[k] = 0.0f;
 
   const UTable<TBL> t{p.seg, tab.cu, tab.off};
   int s_hint = 0;
   const uint32_t row_bytes = W * 2u, half_bytes = d * 2u, slice_bytes = slice * kSlice128 * 2u;
-  constexpr int kParts = kSlice128 * 2 / 16;
-  for (uint32_t n = __builtin_amdgcn_readfirstlane(wg_in_slice); n < N; n += per_slice) {
+  const uint32_t lane_off = lane * 2u;
+  constexpr int kParts = kSlice128 * 2 / 16;   // 16-byte parts of a row slice
+  uint32_t set = 0;
+  for (uint32_t n = __builtin_amdgcn_readfirstlane(wg_in_slice); n < N; n += per_slice, set ^= 1u) {
     const Row128 row = row128<TBL>(n, s_hint, t, p.seg.S);
-    stage_window128<CO>(stage, rsc, rkv, row, row_bytes, half_bytes, slice_bytes, p.io_bytes);
-    const float g = elem<1>(load_pack<1>(rdo, (n * d + col) * 2u), 0);
-    __syncthreads();
-    const bool present = !(CO == 2 && wave < 2 && !row.has_prev);
-    uint16_t* ss = stage + (wave * kChunk128) * kSlice128 + lane;
-    uint16_t* sv = stage + (Wn::kRows + wave * kChunk128) * kSlice128 + lane;
-    float e[kChunk128];
-    float m = 0.0f;
+    const bool present = wv.present(row);
+    const uint32_t b = wv.base(row, row_bytes, half_bytes, slice_bytes);
+    const float g = __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rdo, (n * d + col) * 2u, 0, 0)) << 16);
+    float x[K];
+    uint32_t v[K];
     if (present) {
+      uint32_t sc[K];
 #pragma unroll
-      for (int k = 0; k < kChunk128; ++k) e[k] = __uint_as_float(uint32_t(ss[k * kSlice128]) << 16) + ape_r[k];
-      m = e[0];
+      for (int k = 0; k < K; ++k) sc[k] = __builtin_amdgcn_raw_buffer_load_b16(rsc, lane_off, b + k * row_bytes, kAuxStream);
 #pragma unroll
-      for (int k = 1; k < kChunk128; ++k) m = fmaxf(m, e[k]);
+      for (int k = 0; k < K; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b16(rkv, lane_off, b + k * row_bytes, kAuxStream);
+#pragma unroll
+      for (int k = 0; k < K; ++k) x[k] = __uint_as_float(sc[k] << 16) + ape_w[k * kSlice128];
+    } else {
+#pragma unroll
+      for (int k = 0; k < K; ++k) { x[k] = 0.0f; v[k] = 0u; }
     }
-    const int first = (CO == 2 && !row.has_prev) ? 2 : 0;
-    red[wave * 64 + lane] = m;
-    __syncthreads();
-    m = red[first * 64 + lane];
-    for (int w = first + 1; w < Wn::kChunks; ++w) m = fmaxf(m, red[w * 64 + lane]);
-    float zc = 0.0f, ac = 0.0f;
-    if (present) {
-#pragma unroll
-      for (int k = 0; k < kChunk128; ++k) e[k] = csa_exp(e[k] - m);
-      zc = e[0];
-#pragma unroll
-      for (int k = 1; k < kChunk128; ++k) zc = zc + e[k];
-#pragma unroll
-      for (int k = 0; k < kChunk128; ++k) ac = __builtin_fmaf(e[k], __uint_as_float(uint32_t(sv[k * kSlice128]) << 16), ac);
-    }
-    red[(Wn::kChunks + wave) * 64 + lane] = zc;
-    red[(2 * Wn::kChunks + wave) * 64 + lane] = ac;
-    __syncthreads();
-    // every wave merges the chunks in the same order
-    float Z = red[(Wn::kChunks + first) * 64 + lane], acc = red[(2 * Wn::kChunks + first) * 64 + lane];
-    for (int w = first + 1; w < Wn::kChunks; ++w) {
-      Z = Z + red[(Wn::kChunks + w) * 64 + lane];
-      acc = acc + red[(2 * Wn::kChunks + w) * 64 + lane];
-    }
+    float Z, acc;
+    softmax128<CO>(x, v, present, row.has_prev, wave, lane, wv, red + set * Wn::kRedFloats, Z, acc);
     const float R = 1.0f / Z;
     const float o = acc * R;
     const float G = R * g;
     if (present) {
 #pragma unroll
-      for (int k = 0; k < kChunk128; ++k) {
-        const float v = __uint_as_float(uint32_t(sv[k * kSlice128]) << 16);
-        const float a = e[k] * G;
-        const float ds = a * (v - o);
+      for (int k = 0; k < K; ++k) {
+        const float a = x[k] * G;
+        const float ds = a * (__uint_as_float(v[k] << 16) - o);
         dape_r[k] += ds;
         const uint32_t ab = pack_bf16x2(a, ds);
-        sv[k * kSlice128] = static_cast<uint16_t>(ab & 0xFFFFu);  // dKV over kv
-        ss[k * kSlice128] = static_cast<uint16_t>(ab >> 16);      // dScore over score
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(ab & 0xFFFFu), rdkv, lane_off, b + k * row_bytes,
+                                              kAuxStreamStore);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(ab >> 16), rdsc, lane_off, b + k * row_bytes,
+                                              kAuxStreamStore);
       }
-    }
-    __syncthreads();
-    // store the gradient slices where the window came from (masked rows: none)
-    for (int q = threadIdx.x; q < 2 * Wn::kRows * kParts; q += NT) {
-      const int part = q % kParts, rq = q / kParts;
-      const int tensor = rq / Wn::kRows, k = rq % Wn::kRows;
-      const uint32_t o2 = row128_offset<CO>(k, row.own, CO == 2 && row.has_prev, row_bytes, half_bytes, slice_bytes,
-                                            p.io_bytes);
-      if (o2 == p.io_bytes) continue;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + (tensor * Wn::kRows + k) * kSlice128 + part * 8);
-      __builtin_amdgcn_raw_buffer_store_b128(v, tensor ? rdkv : rdsc, o2 + part * 16u, 0, kAuxStreamStore);
     }
     if (row.last) {
       // the segment's last block owns the never-read slots next to it: its
@@ -1374,15 +1375,14 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void bwd128_kernel(Bwd128Para
         __builtin_amdgcn_raw_buffer_store_b128(z, tensor ? rdkv : rdsc, o2 + part * 16u, 0, kAuxStreamStore);
       }
     }
-    __syncthreads();  // the next row's staging overwrites stage and red
   }
   // dAPE: one partial row per workgroup of a slice (column-block layout)
   const uint32_t prow = p.partial_rows;
   const uint32_t nblk = (kRatio128 * W + kPartBlock - 1) / kPartBlock;
   const rsrc_t rpart = make_rsrc(p.partials, nblk * prow * kPartBlock * 4u);
 #pragma unroll
-  for (int k = 0; k < kChunk128; ++k) {
-    const uint32_t j = (pos0 + k) * W + half * d + col;
+  for (int k = 0; k < K; ++k) {
+    const uint32_t j = (wv.pos0 + k) * W + wv.half * d + col;
     const uint32_t o2 = ((j / kPartBlock) * prow + wg_in_slice) * kPartBlock + (j % kPartBlock);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dape_r[k]), rpart, o2 * 4u, 0, 0);
   }
