@@ -210,7 +210,9 @@ Plan make_plan_r128(const Problem& p) {
   const int NT = 2 * chunks * 64;                      // two waves per 64-entry chunk
   // two exchange sets: wave maxima, part-0 chains, chunk sums
   const uint64_t red_bytes = 2ull * (2 * chunks * 64 + 4 * chunks * 64) * 4;
-  const uint64_t ape_bytes = uint64_t(rows) * csa::kSlice128 * 4;   // backward: APE slice
+  const uint64_t stage_bytes = 2ull * rows * csa::kSlice128 * 2;   // staged window (score, kv)
+  // the staged window follows the table in LDS and is accessed 16 bytes at a
+  // time: keep it 16-byte aligned
   const uint32_t table_words =
       pl.global_table ? 0 : static_cast<uint32_t>(align_up(2 * (NT / 64) + 2 * uint64_t(p.S + 1), 4));
   pl.nslices = static_cast<uint32_t>(p.head_dim / csa::kSlice128);
@@ -227,7 +229,7 @@ Plan make_plan_r128(const Problem& p) {
     pl.fwd.threads = NT;
     pl.fwd.cols = 1;
     pl.fwd_lds_table_words = table_words;
-    pl.fwd.lds_bytes = table_words * 4ull + red_bytes;
+    pl.fwd.lds_bytes = table_words * 4ull + stage_bytes + red_bytes;
     pl.ws_fwd = pl.global_table ? kHeaderBytes + pl.off_bytes : 0;
   }
   {
@@ -250,7 +252,7 @@ Plan make_plan_r128(const Problem& p) {
     pl.bwd_main_wgs = static_cast<uint32_t>(main);
     pl.partial_rows = static_cast<uint32_t>(per);
     pl.lds_table_words = table_words;
-    pl.bwd.lds_bytes = table_words * 4ull + ape_bytes + red_bytes;
+    pl.bwd.lds_bytes = table_words * 4ull + stage_bytes + red_bytes;
     pl.partial_offset = kHeaderBytes + pl.off_bytes;
     const uint64_t nblk = (uint64_t(p.ratio) * W + csa::kPartBlock - 1) / csa::kPartBlock;
     pl.ws_bwd = pl.partial_offset + align_up(nblk * pl.partial_rows * csa::kPartBlock * 4, 256);

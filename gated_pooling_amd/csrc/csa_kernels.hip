@@ -1078,25 +1078,25 @@ __global__ __launch_bounds__(kReduceNT) void dape_reduce_kernel(ReduceParams p) 
 // ---------------------------------------------------------------------------
 // ratio = 128 [PR5984: ratio=128 commit]: a window holds 128 * coff rows per
 // column, too many for one lane's registers.  A workgroup owns a slice of
-// kSlice128 columns (lane = column) and walks output rows.  Each 64-entry
-// summation chunk of the window is held by two waves, 32 entries each
-// (`part` 0 and 1), so a lane keeps 32 window entries and every 16-bit load
-// and store of a wave covers one 128-byte line of one row.  Per row:
-//   1. each wave loads its 32 score and kv entries straight into registers;
-//      x = score + ape, the wave's max, exchanged through LDS -> window max m;
+// kSlice128 columns (lane = column) and walks output rows.  The window's row
+// slices (score and kv, 128 bytes each) are staged in LDS with 16-byte loads,
+// and each 64-entry summation chunk is held by two waves, 32 entries each
+// (`part` 0 and 1).  Per row:
+//   1. x = score + ape for the wave's 32 entries, the wave's max, exchanged
+//      through LDS -> window max m;
 //   2. e = EXP(x - m); part 0 starts the chunk's Z (from its first e) and acc
 //      (fma chain from 0), part 1 continues both chains from part 0's values
 //      (handed over through LDS), so every chunk is summed in entry order;
 //      the chunk sums are then added in chunk order: exactly the chunked fp32
 //      order of windows above 64 entries (the first block at coff 2 has only
 //      the own half: chunks 2 and 3);
-//   backward 3. a = e * R * g, ds = a (v - o), bf16 results stored to the
-//      slots the window came from; dAPE sums stay in registers (a wave always
-//      holds the same 32 positions of its slice) and leave as one partial row
-//      per workgroup.
-// LDS holds only the exchange buffers (two sets, alternating between rows)
-// and, in the backward, the workgroup's APE slice.  head_dim is a multiple of
-// kSlice128, so every row slice is whole.
+//   backward 3. a = e * R * g, ds = a (v - o), bf16 results written over the
+//      staged inputs in LDS, then stored with 16-byte stores; dAPE sums stay
+//      in registers (a wave always holds the same 32 positions of its slice)
+//      and leave as one partial row per workgroup.
+// The forward loads the next row's window into registers while the current
+// row computes.  head_dim is a multiple of kSlice128, so every row slice is
+// whole.
 // ---------------------------------------------------------------------------
 template <int CO>
 struct Win128 {
@@ -1105,10 +1105,24 @@ struct Win128 {
   static constexpr int kPart = kChunk128 / 2;         // entries per wave
   static constexpr int kWaves = 2 * kChunks;
   static constexpr int kThreads = kWaves * 64;
+  static constexpr int kStageBytes = 2 * kRows * kSlice128 * 2;  // score, kv as bf16
   // one exchange set: wave maxima [kWaves][64], part-0 chains [2][kChunks][64],
   // chunk sums [2][kChunks][64]
   static constexpr int kRedFloats = kWaves * 64 + 4 * kChunks * 64;
 };
+
+// Byte offset in kv/score of window row k's slice, or `oob` when the row is
+// masked (the previous half of a segment's first block).
+template <int CO>
+__device__ __forceinline__ uint32_t row128_offset(int k, uint32_t own, bool has_prev, uint32_t row_bytes,
+                                                  uint32_t half_bytes, uint32_t slice_bytes, uint32_t oob) {
+  if constexpr (CO == 2) {
+    if (k < kRatio128) return has_prev ? (own - kRatio128 + k) * row_bytes + slice_bytes : oob;
+    return (own + k - kRatio128) * row_bytes + half_bytes + slice_bytes;
+  } else {
+    return (own + k) * row_bytes + slice_bytes;
+  }
+}
 
 // Row of output row n (uniform): segment lookup on the scalar unit.
 struct Row128 {
@@ -1132,34 +1146,74 @@ __device__ __forceinline__ Row128 row128(uint32_t n, int& s_hint, const UTable<T
   return r;
 }
 
+// A thread's share of one staged window: kIters 16-byte parts; iterations
+// [0, kIters/2) are score rows, the rest kv rows, so the buffer resource of
+// each load is known at compile time.
+template <int CO>
+struct Stage128 {
+  static constexpr int kParts = kSlice128 * 2 / 16;  // 16-byte parts of a row slice
+  static constexpr int kIters = 2 * Win128<CO>::kRows * kParts / Win128<CO>::kThreads;
+  static constexpr int kRowsPerIter = Win128<CO>::kThreads / kParts;
+  static_assert(2 * Win128<CO>::kRows * kParts % Win128<CO>::kThreads == 0, "whole iterations");
+  u32x4 v[kIters];
+  // window row and tensor of iteration it for this thread
+  __device__ static __forceinline__ int row_of(int it) {
+    return static_cast<int>(threadIdx.x / kParts) + (it % (kIters / 2)) * kRowsPerIter;
+  }
+};
+
+// Issue every load of a thread's share of the window (no wait).
+template <int CO>
+__device__ __forceinline__ void issue_window128(Stage128<CO>& st, rsrc_t rsc, rsrc_t rkv, const Row128& row,
+                                                uint32_t row_bytes, uint32_t half_bytes, uint32_t slice_bytes,
+                                                uint32_t oob) {
+  using S = Stage128<CO>;
+  const uint32_t part = threadIdx.x % S::kParts;
+#pragma unroll
+  for (int it = 0; it < S::kIters; ++it) {
+    const uint32_t o = row128_offset<CO>(S::row_of(it), row.own, CO == 2 && row.has_prev, row_bytes, half_bytes,
+                                         slice_bytes, oob);
+    st.v[it] = __builtin_amdgcn_raw_buffer_load_b128(it < S::kIters / 2 ? rsc : rkv, o == oob ? oob : o + part * 16u,
+                                                     0, kAuxStream);
+  }
+}
+
+// Write a thread's share of the window into LDS (waits for its loads).
+template <int CO>
+__device__ __forceinline__ void write_window128(uint16_t* stage, const Stage128<CO>& st) {
+  using S = Stage128<CO>;
+  const int part = threadIdx.x % S::kParts;
+#pragma unroll
+  for (int it = 0; it < S::kIters; ++it) {
+    const int rq = (it / (S::kIters / 2)) * Win128<CO>::kRows + S::row_of(it);
+    *reinterpret_cast<u32x4*>(stage + rq * kSlice128 + part * 8) = st.v[it];
+  }
+}
+
 // A wave's place in the window: chunk, part, half and first block position.
 template <int CO>
 struct Wave128 {
   int chunk, part, half;
   uint32_t pos0;        // block position of the wave's first entry
+  uint32_t k0;          // window row of the wave's first entry
   __device__ __forceinline__ explicit Wave128(int wave) {
     chunk = wave >> 1;
     part = wave & 1;
     half = (CO == 2) ? (chunk >> 1) : 0;
     pos0 = (chunk & 1) * kChunk128 + part * Win128<CO>::kPart;
-  }
-  // byte offset of the wave's first entry's row slice in kv/score (uniform)
-  __device__ __forceinline__ uint32_t base(const Row128& row, uint32_t row_bytes, uint32_t half_bytes,
-                                           uint32_t slice_bytes) const {
-    const uint32_t r0 = (CO == 2 && half == 0) ? row.own - kRatio128 + pos0 : row.own + pos0;
-    return r0 * row_bytes + ((CO == 2 && half == 1) ? half_bytes : 0u) + slice_bytes;
+    k0 = half * kRatio128 + pos0;
   }
   // the previous-half waves of a segment's first block have no entries
   __device__ __forceinline__ bool present(const Row128& row) const { return !(CO == 2 && half == 0 && !row.has_prev); }
 };
 
 // Window max and chunk sums through one exchange set.  x holds the wave's
-// logits on entry and its e = EXP(x - m) on return; Z/acc are the window's.
-// Returns false (and leaves Z/acc unset) for lanes of absent waves.
+// logits on entry and its e = EXP(x - m) on return; sv points at the wave's
+// first staged kv entry (stride kSlice128); Z/acc are the window's.
 template <int CO>
-__device__ __forceinline__ void softmax128(float (&x)[Win128<CO>::kPart], const uint32_t (&v)[Win128<CO>::kPart],
-                                           bool present, bool has_prev, int wave, int lane, const Wave128<CO>& wv,
-                                           float* red, float& Z, float& acc) {
+__device__ __forceinline__ void softmax128(float (&x)[Win128<CO>::kPart], const uint16_t* sv, bool present,
+                                           bool has_prev, int wave, int lane, const Wave128<CO>& wv, float* red,
+                                           float& Z, float& acc) {
   using Wn = Win128<CO>;
   constexpr int K = Wn::kPart;
   float* rm = red;                                  // [kWaves][64]
@@ -1177,16 +1231,18 @@ __device__ __forceinline__ void softmax128(float (&x)[Win128<CO>::kPart], const 
   __syncthreads();
   float m = rm[first_w * 64 + lane];
   for (int w = first_w + 1; w < Wn::kWaves; ++w) m = fmaxf(m, rm[w * 64 + lane]);
+  if (present) {
 #pragma unroll
-  for (int k = 0; k < K; ++k) x[k] = csa_exp(x[k] - m);
-  if (present && wv.part == 0) {
-    float zc = x[0], ac = 0.0f;
+    for (int k = 0; k < K; ++k) x[k] = csa_exp(x[k] - m);
+    if (wv.part == 0) {
+      float zc = x[0], ac = 0.0f;
 #pragma unroll
-    for (int k = 1; k < K; ++k) zc = zc + x[k];
+      for (int k = 1; k < K; ++k) zc = zc + x[k];
 #pragma unroll
-    for (int k = 0; k < K; ++k) ac = __builtin_fmaf(x[k], __uint_as_float(v[k] << 16), ac);
-    rz0[wv.chunk * 64 + lane] = zc;
-    ra0[wv.chunk * 64 + lane] = ac;
+      for (int k = 0; k < K; ++k) ac = __builtin_fmaf(x[k], __uint_as_float(uint32_t(sv[k * kSlice128]) << 16), ac);
+      rz0[wv.chunk * 64 + lane] = zc;
+      ra0[wv.chunk * 64 + lane] = ac;
+    }
   }
   __syncthreads();
   if (present && wv.part == 1) {
@@ -1194,7 +1250,7 @@ __device__ __forceinline__ void softmax128(float (&x)[Win128<CO>::kPart], const 
 #pragma unroll
     for (int k = 0; k < K; ++k) zc = zc + x[k];
 #pragma unroll
-    for (int k = 0; k < K; ++k) ac = __builtin_fmaf(x[k], __uint_as_float(v[k] << 16), ac);
+    for (int k = 0; k < K; ++k) ac = __builtin_fmaf(x[k], __uint_as_float(uint32_t(sv[k * kSlice128]) << 16), ac);
     rz[wv.chunk * 64 + lane] = zc;
     ra[wv.chunk * 64 + lane] = ac;
   }
@@ -1217,7 +1273,9 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void fwd128_kernel(Fwd128Para
   if constexpr (TBL != kTableArgs) {
     if (!load_segment_table<kRatio128, NT, TBL>(p.seg, lds, tab)) return;
   }
-  float* red = reinterpret_cast<float*>(lds + p.lds_table_words);  // two exchange sets
+  // LDS: [table][staged window][two exchange sets]
+  uint16_t* stage = reinterpret_cast<uint16_t*>(lds + p.lds_table_words);
+  float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(stage) + Wn::kStageBytes);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const Wave128<CO> wv(wave);
@@ -1233,43 +1291,50 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void fwd128_kernel(Fwd128Para
   for (int k = 0; k < K; ++k)
     ape_r[k] = __uint_as_float(
         __builtin_amdgcn_raw_buffer_load_b32(rape, ((wv.pos0 + k) * W + wv.half * d + col) * 4u, 0, 0));
+  const uint16_t* ss = stage + wv.k0 * kSlice128 + lane;
+  const uint16_t* sv = stage + (Wn::kRows + wv.k0) * kSlice128 + lane;
 
   const UTable<TBL> t{p.seg, tab.cu, tab.off};
   int s_hint = 0;
   const uint32_t row_bytes = W * 2u, half_bytes = d * 2u, slice_bytes = slice * kSlice128 * 2u;
-  const uint32_t lane_off = lane * 2u;
+  // The next row's window is loaded into registers while this row computes.
+  Stage128<CO> st;
+  uint32_t n = __builtin_amdgcn_readfirstlane(blockIdx.x / nslices);
+  Row128 row{};
+  if (n < N) {
+    row = row128<TBL>(n, s_hint, t, p.seg.S);
+    issue_window128<CO>(st, rsc, rkv, row, row_bytes, half_bytes, slice_bytes, p.io_bytes);
+  }
   uint32_t set = 0;
-  for (uint32_t n = __builtin_amdgcn_readfirstlane(blockIdx.x / nslices); n < N; n += per_slice, set ^= 1u) {
-    const Row128 row = row128<TBL>(n, s_hint, t, p.seg.S);
+  for (; n < N; n += per_slice, set ^= 1u) {
+    write_window128<CO>(stage, st);
+    __syncthreads();
+    const uint32_t nn = n + per_slice;
+    Row128 nrow{};
+    if (nn < N) {
+      nrow = row128<TBL>(nn, s_hint, t, p.seg.S);
+      issue_window128<CO>(st, rsc, rkv, nrow, row_bytes, half_bytes, slice_bytes, p.io_bytes);
+    }
     const bool present = wv.present(row);
     float x[K];
-    uint32_t v[K];
-    if (present) {
-      const uint32_t b = wv.base(row, row_bytes, half_bytes, slice_bytes);
-      uint32_t sc[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) sc[k] = __builtin_amdgcn_raw_buffer_load_b16(rsc, lane_off, b + k * row_bytes, kAuxStream);
-#pragma unroll
-      for (int k = 0; k < K; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b16(rkv, lane_off, b + k * row_bytes, kAuxStream);
-#pragma unroll
-      for (int k = 0; k < K; ++k) x[k] = __uint_as_float(sc[k] << 16) + ape_r[k];
-    } else {
-#pragma unroll
-      for (int k = 0; k < K; ++k) { x[k] = 0.0f; v[k] = 0u; }
-    }
+    for (int k = 0; k < K; ++k) x[k] = __uint_as_float(uint32_t(ss[k * kSlice128]) << 16) + ape_r[k];
     float Z, acc;
-    softmax128<CO>(x, v, present, row.has_prev, wave, lane, wv, red + set * Wn::kRedFloats, Z, acc);
+    // every read of the staged window happens before softmax128's last barrier
+    softmax128<CO>(x, sv, present, row.has_prev, wave, lane, wv, red + set * Wn::kRedFloats, Z, acc);
     if (wave == 0) {
       const float o = acc * (1.0f / Z);
       const Pack<1> ob{{pack_bf16x2(o, 0.0f)}};
       store_pack<1>(rout, (n * d + col) * 2u, ob);
     }
+    row = nrow;
   }
 }
 
 template <int CO, int TBL>
 __global__ __launch_bounds__(Win128<CO>::kThreads) void bwd128_kernel(Bwd128Params p) {
   using Wn = Win128<CO>;
+  using S = Stage128<CO>;
   constexpr int NT = Wn::kThreads, K = Wn::kPart;
   extern __shared__ int32_t lds[];
   SegTable tab{nullptr, nullptr};
@@ -1285,9 +1350,9 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void bwd128_kernel(Bwd128Para
     zero_sweep<kRatio128, CO, NT>(p, tab);
     return;
   }
-  // LDS: [table][APE slice: kRows x 64 fp32][two exchange sets]
-  float* ape_s = reinterpret_cast<float*>(lds + p.lds_table_words);
-  float* red = ape_s + Wn::kRows * kSlice128;
+  // LDS: [table][staged window][two exchange sets]
+  uint16_t* stage = reinterpret_cast<uint16_t*>(lds + p.lds_table_words);
+  float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(stage) + Wn::kStageBytes);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const Wave128<CO> wv(wave);
@@ -1301,60 +1366,63 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void bwd128_kernel(Bwd128Para
   const rsrc_t rdsc = make_rsrc(p.dscore, p.io_bytes);
   const rsrc_t rape = make_rsrc(p.ape, kRatio128 * W * 4u);
   const rsrc_t rdo = make_rsrc(p.dout, N * d * 2u);
-  // APE slice: entry (half, position) of the window at ape_s[(half * 128 + pos) * 64 + lane]
-  for (int q = threadIdx.x; q < Wn::kRows * kSlice128; q += NT) {
-    const uint32_t hp = q / kSlice128, c = q % kSlice128, h = hp / kRatio128, pos = hp % kRatio128;
-    ape_s[q] = __uint_as_float(
-        __builtin_amdgcn_raw_buffer_load_b32(rape, (pos * W + h * d + slice * kSlice128 + c) * 4u, 0, 0));
-  }
-  __syncthreads();
-  const float* ape_w = ape_s + (wv.half * kRatio128 + wv.pos0) * kSlice128 + lane;
-  float dape_r[K];
+  float ape_r[K], dape_r[K];
 #pragma unroll
-  for (int k = 0; k < K; ++k) dape_r[k] = 0.0f;
+  for (int k = 0; k < K; ++k) {
+    ape_r[k] = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rape, ((wv.pos0 + k) * W + wv.half * d + col) * 4u, 0, 0));
+    dape_r[k] = 0.0f;
+  }
+  uint16_t* ss = stage + wv.k0 * kSlice128 + lane;
+  uint16_t* sv = stage + (Wn::kRows + wv.k0) * kSlice128 + lane;
 
   const UTable<TBL> t{p.seg, tab.cu, tab.off};
   int s_hint = 0;
   const uint32_t row_bytes = W * 2u, half_bytes = d * 2u, slice_bytes = slice * kSlice128 * 2u;
-  const uint32_t lane_off = lane * 2u;
-  constexpr int kParts = kSlice128 * 2 / 16;   // 16-byte parts of a row slice
+  const uint32_t spart = threadIdx.x % S::kParts;
   uint32_t set = 0;
   for (uint32_t n = __builtin_amdgcn_readfirstlane(wg_in_slice); n < N; n += per_slice, set ^= 1u) {
     const Row128 row = row128<TBL>(n, s_hint, t, p.seg.S);
-    const bool present = wv.present(row);
-    const uint32_t b = wv.base(row, row_bytes, half_bytes, slice_bytes);
-    const float g = __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rdo, (n * d + col) * 2u, 0, 0)) << 16);
-    float x[K];
-    uint32_t v[K];
-    if (present) {
-      uint32_t sc[K];
-#pragma unroll
-      for (int k = 0; k < K; ++k) sc[k] = __builtin_amdgcn_raw_buffer_load_b16(rsc, lane_off, b + k * row_bytes, kAuxStream);
-#pragma unroll
-      for (int k = 0; k < K; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b16(rkv, lane_off, b + k * row_bytes, kAuxStream);
-#pragma unroll
-      for (int k = 0; k < K; ++k) x[k] = __uint_as_float(sc[k] << 16) + ape_w[k * kSlice128];
-    } else {
-#pragma unroll
-      for (int k = 0; k < K; ++k) { x[k] = 0.0f; v[k] = 0u; }
+    {
+      Stage128<CO> st;
+      issue_window128<CO>(st, rsc, rkv, row, row_bytes, half_bytes, slice_bytes, p.io_bytes);
+      write_window128<CO>(stage, st);
     }
+    const float g = __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rdo, (n * d + col) * 2u, 0, 0)) << 16);
+    __syncthreads();
+    const bool present = wv.present(row);
+    float x[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) x[k] = __uint_as_float(uint32_t(ss[k * kSlice128]) << 16) + ape_r[k];
     float Z, acc;
-    softmax128<CO>(x, v, present, row.has_prev, wave, lane, wv, red + set * Wn::kRedFloats, Z, acc);
+    softmax128<CO>(x, sv, present, row.has_prev, wave, lane, wv, red + set * Wn::kRedFloats, Z, acc);
     const float R = 1.0f / Z;
     const float o = acc * R;
     const float G = R * g;
     if (present) {
 #pragma unroll
       for (int k = 0; k < K; ++k) {
+        const float v = __uint_as_float(uint32_t(sv[k * kSlice128]) << 16);
         const float a = x[k] * G;
-        const float ds = a * (__uint_as_float(v[k] << 16) - o);
+        const float ds = a * (v - o);
         dape_r[k] += ds;
         const uint32_t ab = pack_bf16x2(a, ds);
-        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(ab & 0xFFFFu), rdkv, lane_off, b + k * row_bytes,
-                                              kAuxStreamStore);
-        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(ab >> 16), rdsc, lane_off, b + k * row_bytes,
-                                              kAuxStreamStore);
+        sv[k * kSlice128] = static_cast<uint16_t>(ab & 0xFFFFu);  // dKV over kv
+        ss[k * kSlice128] = static_cast<uint16_t>(ab >> 16);      // dScore over score
       }
+    }
+    __syncthreads();
+    // store the gradient slices where the window came from (masked rows: none)
+#pragma unroll
+    for (int it = 0; it < S::kIters; ++it) {
+      const int k = S::row_of(it);
+      const uint32_t o2 = row128_offset<CO>(k, row.own, CO == 2 && row.has_prev, row_bytes, half_bytes, slice_bytes,
+                                            p.io_bytes);
+      const int rq = (it / (S::kIters / 2)) * Wn::kRows + k;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rq * kSlice128 + spart * 8);
+      if (o2 != p.io_bytes)
+        __builtin_amdgcn_raw_buffer_store_b128(v, it < S::kIters / 2 ? rdsc : rdkv, o2 + spart * 16u, 0,
+                                               kAuxStreamStore);
     }
     if (row.last) {
       // the segment's last block owns the never-read slots next to it: its
@@ -1362,8 +1430,8 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void bwd128_kernel(Bwd128Para
       const u32x4 z = {0u, 0u, 0u, 0u};
       const uint32_t tail = row.seg_end - (row.own + kRatio128);
       const uint32_t nz = (CO == 2 ? kRatio128 : 0) + tail * CO;   // row slices to zero
-      for (uint32_t q = threadIdx.x; q < 2 * nz * kParts; q += NT) {
-        const uint32_t part = q % kParts, rq = q / kParts;
+      for (uint32_t q = threadIdx.x; q < 2 * nz * S::kParts; q += NT) {
+        const uint32_t part = q % S::kParts, rq = q / S::kParts;
         const uint32_t tensor = rq / nz, k = rq % nz;
         uint32_t o2;
         if (CO == 2 && k < kRatio128) {
@@ -1375,6 +1443,7 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void bwd128_kernel(Bwd128Para
         __builtin_amdgcn_raw_buffer_store_b128(z, tensor ? rdkv : rdsc, o2 + part * 16u, 0, kAuxStreamStore);
       }
     }
+    __syncthreads();  // the next row's staging overwrites stage
   }
   // dAPE: one partial row per workgroup of a slice (column-block layout)
   const uint32_t prow = p.partial_rows;
