@@ -218,9 +218,8 @@ Plan make_plan_r128(const Problem& p) {
   pl.nslices = static_cast<uint32_t>(p.head_dim / csa::kSlice128);
   const int64_t out_rows = p.N > 0 ? p.N : 1;
   {
-    // measured on 65536-token packs: the forward keeps 4 waves per SIMD at
-    // either coff, the backward 2 (one 512-thread workgroup per CU at coff 2,
-    // two 256-thread workgroups at coff 1)
+    // the number of workgroups the chip holds at once (measured best on
+    // 65536-token packs): forward 2 per CU at coff 2, 4 at coff 1
     const int cap = tu.r128_fwd_wgs ? tu.r128_fwd_wgs : (p.coff == 2 ? 512 : 1024);
     int64_t per = cap / pl.nslices;
     if (per < 1) per = 1;
@@ -233,7 +232,8 @@ Plan make_plan_r128(const Problem& p) {
     pl.ws_fwd = pl.global_table ? kHeaderBytes + pl.off_bytes : 0;
   }
   {
-    const int cap = tu.r128_bwd_wgs ? tu.r128_bwd_wgs : (p.coff == 2 ? 256 : 512);
+    // backward: 2 per CU at coff 2, 3 at coff 1
+    const int cap = tu.r128_bwd_wgs ? tu.r128_bwd_wgs : (p.coff == 2 ? 512 : 768);
     int64_t per = cap / pl.nslices;
     if (per < 1) per = 1;
     if (per > out_rows) per = out_rows;

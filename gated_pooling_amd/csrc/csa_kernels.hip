@@ -1286,11 +1286,11 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void fwd128_kernel(Fwd128Para
   const rsrc_t rsc = make_rsrc(p.score, p.io_bytes);
   const rsrc_t rape = make_rsrc(p.ape, kRatio128 * W * 4u);
   const rsrc_t rout = make_rsrc(p.out, N * d * 2u);
+  const uint32_t ape_off = (wv.pos0 * W + wv.half * d + col) * 4u;
   float ape_r[K];
 #pragma unroll
   for (int k = 0; k < K; ++k)
-    ape_r[k] = __uint_as_float(
-        __builtin_amdgcn_raw_buffer_load_b32(rape, ((wv.pos0 + k) * W + wv.half * d + col) * 4u, 0, 0));
+    ape_r[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rape, ape_off, k * W * 4u, 0));
   const uint16_t* ss = stage + wv.k0 * kSlice128 + lane;
   const uint16_t* sv = stage + (Wn::kRows + wv.k0) * kSlice128 + lane;
 
@@ -1366,11 +1366,14 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void bwd128_kernel(Bwd128Para
   const rsrc_t rdsc = make_rsrc(p.dscore, p.io_bytes);
   const rsrc_t rape = make_rsrc(p.ape, kRatio128 * W * 4u);
   const rsrc_t rdo = make_rsrc(p.dout, N * d * 2u);
+  // APE: held in registers at coff 1; at coff 2 it is read again for every
+  // row (from the cache), which keeps the kernel at 4 waves per SIMD
+  constexpr bool kApeRegs = CO == 1;
+  const uint32_t ape_off = (wv.pos0 * W + wv.half * d + col) * 4u;
   float ape_r[K], dape_r[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    ape_r[k] = __uint_as_float(
-        __builtin_amdgcn_raw_buffer_load_b32(rape, ((wv.pos0 + k) * W + wv.half * d + col) * 4u, 0, 0));
+    if constexpr (kApeRegs) ape_r[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rape, ape_off, k * W * 4u, 0));
     dape_r[k] = 0.0f;
   }
   uint16_t* ss = stage + wv.k0 * kSlice128 + lane;
@@ -1389,6 +1392,11 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void bwd128_kernel(Bwd128Para
       write_window128<CO>(stage, st);
     }
     const float g = __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rdo, (n * d + col) * 2u, 0, 0)) << 16);
+    if constexpr (!kApeRegs) {
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        ape_r[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rape, ape_off, k * W * 4u, 0));
+    }
     __syncthreads();
     const bool present = wv.present(row);
     float x[K];
