@@ -5,6 +5,7 @@ grid caps, workgroup size, column slice, uniform-row path, prefetch depth)
 once per process, so each configuration runs in a process of its own:
 
     CSA_BWD_PREFETCH=4 python -m tests.tuning_parity
+    CSA_R128_BWD_WGS=5 python -m tests.tuning_parity r128    # ratio-128 packs only
 
 Every case is checked bit for bit (out, dKV, dScore, zero ownership) and
 dAPE to its tolerance, exactly as in the main parity tests.  Prints one line
@@ -37,13 +38,24 @@ def cases():
     yield "random2500_d128_r4_c2", inputs.custom("r2500", lengths, int(sum(lengths)) + 9, 4, 2, 128, seed=4), False
 
 
-def main():
+def cases_r128():
+    """ratio-128 packs: several blocks per segment, tails, a segment shorter
+    than 128, padding rows, both coffs, one and several column slices."""
+    rng = np.random.default_rng(1280)
+    for i, (c, d, nseg) in enumerate(((2, 128, 4), (1, 64, 5), (2, 192, 3), (1, 256, 2))):
+        lengths = rng.integers(0, 900, size=nseg).tolist()
+        lengths[1] = int(rng.integers(1, 128))
+        T = int(sum(lengths)) + int(rng.integers(1, 200))
+        yield f"r128_S{nseg}_c{c}_d{d}", inputs.custom("t128", lengths, T, 128, c, d, seed=60 + i), bool(i % 2)
+
+
+def main(argv):
     if not torch.cuda.is_available():
         print("no GPU", file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
     G.lib()
-    for name, wl, host in cases():
+    for name, wl, host in (cases_r128() if "r128" in argv else cases()):
         cu, T, r, c, d = list(wl.cu_seqlens), wl.total_tokens, wl.ratio, wl.coff, wl.head_dim
         N = G.csa_compressor_total_comp(cu, r)
         kv, sc, ape, dout = inputs.make_tensors(wl, N)
@@ -54,4 +66,4 @@ def main():
 
 
 if __name__ == "__main__":
-    sys.exit(main())
+    sys.exit(main(sys.argv[1:]))
