@@ -62,10 +62,10 @@ csa_status_t ok() {
 
 struct Tuning {
   int fwd_cols = 2;
-  int fwd_max_wgs = 1024;
+  int fwd_max_wgs = 0;    // 0: by ratio (see make_plan)
   int bwd_cols = 2;
   int bwd_threads = 256;
-  int bwd_max_wgs = 256;
+  int bwd_max_wgs = 0;    // 0: by ratio (see make_plan)
   int bwd_slice_bytes = 512;
   int uniform = 1;        // wave-uniform row path where a row has >= 64 chunks
   int fwd_prefetch = 2;   // windows in flight per lane (uniform path)
@@ -275,7 +275,10 @@ Plan make_plan(const Problem& p) {
     const int64_t Gp = pow2_ceil(G);      // lanes of a row
     const int64_t lanes = p.N * Gp;
     int64_t wgs = (lanes + csa::kFwdThreads - 1) / csa::kFwdThreads;
-    if (wgs > tu.fwd_max_wgs) wgs = tu.fwd_max_wgs;
+    // grid cap (measured on the 8192-token packs): 3 workgroups per CU at
+    // ratio 4; ratio 2 windows hold half the bytes and want 4
+    const int64_t cap = tu.fwd_max_wgs ? tu.fwd_max_wgs : (p.ratio >= 4 ? 768 : 1024);
+    if (wgs > cap) wgs = cap;
     if (Gp > csa::kFwdThreads) wgs = align_up(wgs, Gp / csa::kFwdThreads);  // lanes % Gp == 0
     pl.fwd.grid = static_cast<uint32_t>(wgs);
     pl.fwd.threads = csa::kFwdThreads;
@@ -307,7 +310,10 @@ Plan make_plan(const Problem& p) {
     const int64_t slices = Gp / CS;
     const int64_t lanes = p.N * Gp;
     int64_t main = (lanes + NT - 1) / NT;
-    if (main > tu.bwd_max_wgs) main = tu.bwd_max_wgs;
+    // grid cap (measured on the 8192-token packs): one workgroup per CU at
+    // ratio 4; ratio 2 windows hold half the bytes and want 2
+    const int64_t cap = tu.bwd_max_wgs ? tu.bwd_max_wgs : (p.ratio >= 4 ? 256 : 512);
+    if (main > cap) main = cap;
     main = align_up(main, slices);  // whole slices
     // zero-fill workgroups for rows of segments shorter than ratio and rows
     // past cu[S]: at most total_tokens - total_comp*ratio rows qualify

@@ -73,7 +73,8 @@ struct BwdParams {
 
 // ratio = 128 (windows of 128 * coff rows): a workgroup owns a slice of
 // kSlice128 columns (one per lane) and walks output rows; the window slice is
-// staged in LDS and each wave takes one chunk of kChunk128 window entries.
+// staged in LDS and each summation chunk of kChunk128 window entries is held
+// by two waves (half the entries each).
 constexpr int kRatio128 = 128;
 constexpr int kSlice128 = 64;
 constexpr int kChunk128 = 64;
