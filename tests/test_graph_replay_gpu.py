@@ -23,16 +23,27 @@ from tests.test_parity_gpu import NAN_BF16, check_against_oracle
 
 pytestmark = pytest.mark.gpu
 
-T_CAP, R, D = 4608, 4, 128
-# same S = 3 and total_comp = 1000 for every pack; cu[S] and the tails vary
-PACKS = [
-    [1000, 2000, 1000],
-    [1003, 2001, 1002],
-    [4, 3996, 2],
-    [0, 4000, 0],
-    [1, 3, 4003],
-    [2001, 1001, 1003],
-]
+D = 128
+# per ratio: token capacity, total_comp and the packs; the same S = 3 and
+# total_comp for every pack of a ratio, while cu[S] and the tails vary
+CONFIGS = {
+    4: (4608, 1000, [
+        [1000, 2000, 1000],
+        [1003, 2001, 1002],
+        [4, 3996, 2],
+        [0, 4000, 0],
+        [1, 3, 4003],
+        [2001, 1001, 1003],
+    ]),
+    128: (2048, 12, [
+        [512, 768, 256],
+        [520, 800, 300],
+        [127, 1536, 10],
+        [0, 1536, 0],
+        [1, 3, 1600],
+        [1000, 300, 400],
+    ]),
+}
 
 
 @pytest.fixture(scope="module")
@@ -43,10 +54,11 @@ def dev():
     return torch.device("cuda:0")
 
 
+@pytest.mark.parametrize("R", [4, 128])
 @pytest.mark.parametrize("coff", [1, 2])
-def test_graph_replay_with_changing_packs(dev, coff):
+def test_graph_replay_with_changing_packs(dev, coff, R):
+    T_CAP, N, PACKS = CONFIGS[R]
     W = coff * D
-    N = 1000
     S = 3
     for lengths in PACKS:
         assert G.csa_compressor_total_comp(np.concatenate([[0], np.cumsum(lengths)]).tolist(), R) == N
