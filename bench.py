@@ -90,7 +90,8 @@ def load_traffic(kernel, workload):
     return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
-ROLE_OF_KERNEL = (("fwd_kernel", "fwd"), ("bwd_kernel", "bwd_grads"), ("dape_reduce_kernel", "dape_reduce"))
+ROLE_OF_KERNEL = (("fwd_kernel", "fwd"), ("fwd128_kernel", "fwd"), ("bwd_kernel", "bwd_grads"),
+                  ("bwd128_kernel", "bwd_grads"), ("dape_reduce_kernel", "dape_reduce"))
 COPY_BYTES = 512 * 2 ** 20  # the context copy below moves 512 MiB each way
 
 
