@@ -289,6 +289,8 @@ def _r128_cases():
     cases.append((lengths, int(sum(lengths)) + 7, 2, 64, 950, False))
     lengths = rng.integers(0, 260, size=2300).tolist()                   # workspace table
     cases.append((lengths, int(sum(lengths)) + 7, 1, 64, 951, False))
+    cases.append(([300, 260, 7], 600, 2, 1024, 952, True))              # largest head_dim: 16 slices
+    cases.append(([129, 400], 560, 1, 960, 953, False))                 # 15 slices
     return cases
 
 
