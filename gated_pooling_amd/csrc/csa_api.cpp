@@ -22,14 +22,18 @@
 // validated and falls back to the default):
 //   CSA_FWD_COLS      output columns per lane in the forward (2, 4)
 //   CSA_FWD_MAX_WGS   forward grid cap in workgroups of 256 threads
+//                     (default 768 at ratio 4, 1024 at ratio 2)
 //   CSA_BWD_COLS      output columns per lane in the backward (2, 4)
 //   CSA_BWD_THREADS   backward workgroup size (256, 512, 1024)
-//   CSA_BWD_MAX_WGS   backward grid cap (main workgroups)
+//   CSA_BWD_MAX_WGS   backward grid cap in main workgroups (default 256 at
+//                     ratio 4, 512 at ratio 2)
 //   CSA_BWD_SLICE_BYTES  bytes of a half-row one backward workgroup covers
 //                     (>= 128; smaller slices shrink the dAPE partials)
 //   CSA_UNIFORM       1: wave-uniform row path where a row has >= 64 chunks
 //   CSA_FWD_PREFETCH, CSA_BWD_PREFETCH  windows in flight per lane on the
 //                     uniform path (2, 3, 4)
+//   CSA_R128_FWD_WGS, CSA_R128_BWD_WGS  ratio-128 grid caps (default: the
+//                     workgroups the chip holds at once, by coff)
 
 #include <stdarg.h>
 #include <stdio.h>

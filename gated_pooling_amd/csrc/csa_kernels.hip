@@ -10,16 +10,18 @@
 //   * The path is HBM-bound: per consumed kv/score slot it reads 4 bytes and
 //     does ~20 fp32 VALU operations, far from any contraction, so there is no
 //     MFMA.  Every consumed slot is read exactly once.
-//   * Work item = (output row n, chunk of C output columns).  A lane owns one
-//     chunk and walks output rows grid-stride; lanes of a wave take
-//     consecutive chunks, so each wave load covers contiguous bytes of one
-//     half-row (coalesced 16-byte loads for C = 8).
+//   * Work item = (output row n, chunk of C output columns, C in {1, 2, 4}).
+//     A lane owns one chunk and walks output rows grid-stride; lanes of a
+//     wave take consecutive chunks, so each wave load covers contiguous bytes
+//     of one half-row (256 bytes at C = 2).
 //   * At coff = 2 a block's window is the previous block's first-half columns
 //     plus its own second-half columns ([PR5984: fused forward+backward
 //     commit]).  The lane loads exactly those 2*ratio half-row chunks, so no
 //     slot is loaded twice and no block-to-block hand-off is needed.
 //   * The window lives in VGPRs (ratio <= 4 keeps it to 2*4*C bf16 per
-//     tensor); APE for the lane's chunk is loaded once per lane.
+//     tensor); APE for the lane's chunk is loaded once per lane.  Ratio 128
+//     has its own kernels (their section below), which stage each window in
+//     LDS.
 //   * Global memory goes through raw buffer instructions with exact byte
 //     ranges: an index mistake cannot fault, out-of-range loads read 0 and
 //     out-of-range stores are dropped.
