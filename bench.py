@@ -272,7 +272,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (the Compressor path runs on a single "
+        print("bench.py measures one GPU only (the Compressor path runs on a single "
               "device; --gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 

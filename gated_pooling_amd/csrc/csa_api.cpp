@@ -643,7 +643,7 @@ csa_status_t csa_compressor_bwd(const void* kv, const void* score, const float* 
                                 int32_t ratio, int32_t coff, int32_t head_dim, const void* dout, void* dkv,
                                 void* dscore, float* dape, int32_t deterministic, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
-  (void)deterministic;  // this build always reduces dAPE in a fixed order
+  (void)deterministic;  // dAPE is always reduced in a fixed order
   const Problem pr{ratio, coff, head_dim, S, total_tokens, total_comp};
   csa_status_t st = check_problem(pr);
   if (st) return st;

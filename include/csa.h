@@ -167,8 +167,9 @@ csa_status_t csa_compressor_fwd(const void* kv, const void* score, const float* 
  * out/dkv/dscore are deterministic (bit-identical run to run).  dape is
  * reduced in a fixed order and is bit-identical run to run for a given
  * device and problem; `deterministic` is accepted for forward compatibility
- * (0 would permit an unordered reduction) and does not change the result of
- * this build.  total_comp == 0 still writes all zeros to dkv/dscore/dape. */
+ * (0 would permit an unordered reduction) and does not change the result:
+ * the library has only the fixed-order reduction.  total_comp == 0 still
+ * writes all zeros to dkv/dscore/dape. */
 csa_status_t csa_compressor_bwd(const void* kv, const void* score, const float* ape,
                                 const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
                                 int32_t num_segments, int64_t total_tokens, int64_t total_comp,
