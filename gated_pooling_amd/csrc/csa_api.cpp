@@ -341,7 +341,10 @@ Plan make_plan(const Problem& p) {
     pl.bwd_log2_slice = log2i(CS);
     pl.bwd_main_wgs = static_cast<uint32_t>(main);
     pl.partial_rows = static_cast<uint32_t>(main / slices);
-    pl.lds_table_words = pl.global_table ? 0 : static_cast<uint32_t>(2 * (NT / 64) + 2 * (p.S + 1));
+    // the dAPE staging follows the table and is read 16 bytes at a time:
+    // keep it 16-byte aligned
+    pl.lds_table_words =
+        pl.global_table ? 0 : static_cast<uint32_t>(align_up(2 * (NT / 64) + 2 * uint64_t(p.S + 1), 4));
     const uint64_t red_floats = uint64_t(NT) * p.coff * p.ratio * C;  // dAPE staging: every thread's sums
     pl.bwd.lds_bytes = (uint64_t(pl.lds_table_words) + red_floats) * 4;
     pl.partial_offset = kHeaderBytes + pl.off_bytes;

@@ -1009,6 +1009,28 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   const uint32_t prow = p.partial_rows;
   const uint32_t nblk = (R * W + kPartBlock - 1) / kPartBlock;
   const rsrc_t rpart = make_rsrc(p.partials, nblk * prow * kPartBlock * 4u);
+  if (!PAD && (d & 3u) == 0 && (CW & 3u) == 0) {
+    // four consecutive values per step (same order of additions): 16-byte
+    // LDS reads and one 16-byte store, which stays inside one column block
+    // because j is a multiple of 4
+    for (uint32_t idx = threadIdx.x * 4u; idx < QW; idx += NT * 4u) {
+      const uint32_t hi = idx / CW, c = idx - hi * CW;
+      const uint32_t h = hi / R, i = hi - h * R;
+      f32x4 t = *reinterpret_cast<const f32x4*>(stage + idx);
+      for (uint32_t g2 = 1; g2 < RG; ++g2) {
+        const f32x4 u = *reinterpret_cast<const f32x4*>(stage + g2 * QW + idx);
+        t.x = t.x + u.x;
+        t.y = t.y + u.y;
+        t.z = t.z + u.z;
+        t.w = t.w + u.w;
+      }
+      const uint32_t j = i * W + h * d + cbase + c;
+      const uint32_t o = ((j / kPartBlock) * prow + wg_in_slice) * kPartBlock + (j % kPartBlock);
+      const u32x4 v = {__float_as_uint(t.x), __float_as_uint(t.y), __float_as_uint(t.z), __float_as_uint(t.w)};
+      __builtin_amdgcn_raw_buffer_store_b128(v, rpart, o * 4u, 0, 0);
+    }
+    return;
+  }
   for (uint32_t idx = threadIdx.x; idx < QW; idx += NT) {
     const uint32_t hi = idx / CW, c = idx - hi * CW;
     const uint32_t h = hi / R, i = hi - h * R;
