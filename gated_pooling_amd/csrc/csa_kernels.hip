@@ -1012,8 +1012,15 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   if (!PAD && (d & 3u) == 0 && (CW & 3u) == 0) {
     // four consecutive values per step (same order of additions): 16-byte
     // LDS reads and one 16-byte store, which stays inside one column block
-    // because j is a multiple of 4
-    for (uint32_t idx = threadIdx.x * 4u; idx < QW; idx += NT * 4u) {
+    // because j is a multiple of 4.  A thread takes at most CO*R*C/4 steps
+    // (QW = CO*R*C*CS and CS <= NT); the steps are unrolled rather than
+    // looped, so the stores do not make the compiler wait for every
+    // outstanding store of the window loop first (it flushes the memory
+    // counter ahead of a loop that stores).
+#pragma unroll
+    for (int step = 0; step < (CO * R * C + 3) / 4; ++step) {
+      const uint32_t idx = (threadIdx.x + step * NT) * 4u;
+      if (idx >= QW) break;
       const uint32_t hi = idx / CW, c = idx - hi * CW;
       const uint32_t h = hi / R, i = hi - h * R;
       f32x4 t = *reinterpret_cast<const f32x4*>(stage + idx);
