@@ -41,7 +41,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
 METRIC = "fwd+bwd µs/call and HBM GB/s (% of MI355X peak), 3x8192-tok d512 r4 c2"
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_pooling_amd", "csrc", f) for f in
-                  ("csa_kernels.hip", "csa_api.cpp", "csa_launch.h")]
+                  ("csa_kernels.hip", "csa_api.cpp", "csa_launch.h", "csa_walk.h")]
 
 
 def consumed_slots(cu, r, c, d):

@@ -190,6 +190,15 @@ def _stream_ptr(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(stream):
+    """Context under which new tensors are allocated: the launch stream, so
+    the caching allocator does not hand a block that the kernels still use
+    to work on another stream when the local workspace is freed."""
+    import contextlib
+    torch = _torch()
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _dev(t, dtype, name, shape=None):
     torch = _torch()
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -231,11 +240,12 @@ def compressor_fwd(kv, score, ape, cu_seqlens, ratio: int, coff: int, total_comp
     torch = _torch()
     T, d, S = _problem(kv, ape, cu_seqlens, ratio, coff)
     W = coff * d
-    if out is None:
-        out = torch.empty(total_comp, d, dtype=torch.bfloat16, device=kv.device)
     nbytes = csa_compressor_fwd_workspace_size(ratio, coff, d, S, T, total_comp)
-    if ws is None and nbytes:
-        ws = workspace(nbytes, kv.device)
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty(total_comp, d, dtype=torch.bfloat16, device=kv.device)
+        if ws is None and nbytes:
+            ws = workspace(nbytes, kv.device)
     csa_compressor_fwd(_dev(kv, torch.bfloat16, "kv", (T, W)), _dev(score, torch.bfloat16, "score", (T, W)),
                        _dev(ape, torch.float32, "ape", (ratio, W)), _dev(cu_seqlens, torch.int32, "cu_seqlens"),
                        host_cu(cu_seqlens_host), S, T, total_comp, ratio, coff, d, _dev(out, torch.bfloat16, "out", (total_comp, d)),
@@ -250,15 +260,16 @@ def compressor_bwd(kv, score, ape, cu_seqlens, ratio: int, coff: int, total_comp
     torch = _torch()
     T, d, S = _problem(kv, ape, cu_seqlens, ratio, coff)
     W = coff * d
-    if dkv is None:
-        dkv = torch.empty(T, W, dtype=torch.bfloat16, device=kv.device)
-    if dscore is None:
-        dscore = torch.empty(T, W, dtype=torch.bfloat16, device=kv.device)
-    if dape is None:
-        dape = torch.empty(ratio, W, dtype=torch.float32, device=kv.device)
     nbytes = csa_compressor_bwd_workspace_size(ratio, coff, d, S, T, total_comp)
-    if ws is None:
-        ws = workspace(nbytes, kv.device)
+    with _on_stream(stream):
+        if dkv is None:
+            dkv = torch.empty(T, W, dtype=torch.bfloat16, device=kv.device)
+        if dscore is None:
+            dscore = torch.empty(T, W, dtype=torch.bfloat16, device=kv.device)
+        if dape is None:
+            dape = torch.empty(ratio, W, dtype=torch.float32, device=kv.device)
+        if ws is None:
+            ws = workspace(nbytes, kv.device)
     csa_compressor_bwd(_dev(kv, torch.bfloat16, "kv", (T, W)), _dev(score, torch.bfloat16, "score", (T, W)),
                        _dev(ape, torch.float32, "ape", (ratio, W)), _dev(cu_seqlens, torch.int32, "cu_seqlens"),
                        host_cu(cu_seqlens_host), S, T, total_comp, ratio, coff, d, _dev(dout, torch.bfloat16, "dout", (total_comp, d)),

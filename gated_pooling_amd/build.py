@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa.so")
 SOURCES = [os.path.join(CSRC, "csa_kernels.hip"), os.path.join(CSRC, "csa_api.cpp")]
-HEADERS = [os.path.join(CSRC, "csa_launch.h"), os.path.join(ROOT, "include", "csa.h")]
+HEADERS = [os.path.join(CSRC, "csa_launch.h"), os.path.join(CSRC, "csa_walk.h"), os.path.join(ROOT, "include", "csa.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

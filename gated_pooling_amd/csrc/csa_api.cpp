@@ -28,7 +28,9 @@
 //   CSA_BWD_MAX_WGS   backward grid cap in main workgroups (default 256 at
 //                     ratio 4, 512 at ratio 2)
 //   CSA_BWD_SLICE_BYTES  bytes of a half-row one backward workgroup covers
-//                     (>= 128; smaller slices shrink the dAPE partials)
+//                     (>= 128; smaller slices shrink the dAPE partials); the
+//                     chunk count it gives is rounded down to a power of two,
+//                     the only slice shape the kernels' lane mapping supports
 //   CSA_UNIFORM       1: wave-uniform row path where a row has >= 64 chunks
 //   CSA_FWD_PREFETCH, CSA_BWD_PREFETCH  windows in flight per lane on the
 //                     uniform path (2, 3, 4)
@@ -199,6 +201,11 @@ int64_t pow2_ceil(int64_t x) {
   while (p < x) p <<= 1;
   return p;
 }
+int64_t pow2_floor(int64_t x) {
+  int64_t p = 1;
+  while (2 * p <= x) p <<= 1;
+  return p;
+}
 
 // ratio 128: a workgroup per (column slice, group of output rows), the
 // window slice staged in LDS (see the kernels).  Grids are capped at the
@@ -311,6 +318,7 @@ Plan make_plan(const Problem& p) {
     if (CS < 64 / C) CS = 64 / C;
     if (CS > Gp) CS = Gp;
     if (CS > NT) CS = NT;
+    CS = pow2_floor(CS);  // the kernels take log2(CS): slices, partial rows and lanes must agree
     const int64_t slices = Gp / CS;
     const int64_t lanes = p.N * Gp;
     int64_t main = (lanes + NT - 1) / NT;

@@ -51,6 +51,7 @@
 #include <type_traits>
 
 #include "csa_launch.h"
+#include "csa_walk.h"
 
 namespace csa {
 namespace {
@@ -182,7 +183,7 @@ __device__ __forceinline__ uint32_t pack_group_at(const float (&a)[NG][K], int i
 // EXP: the fixed fp32 exponential of the evaluation order.
 //   y >= -104 (clamp; e^-104 is below half the smallest subnormal),
 //   k = rint(y log2 e), r = y - k ln2 in two fma steps (Cody-Waite with
-//   ln2 split as fp32(ln2) + fp32(ln2 - fp32(ln2))), e^r by its degree-6
+//   ln2 split as fp32(ln2) + fp32(ln2 - fp32(ln2))), e^r by its degree-7
 //   Taylor polynomial (Horner, coefficients fp32(1/n!)), scaled by 2^k.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float csa_exp(float y) {
@@ -193,7 +194,8 @@ __device__ __forceinline__ float csa_exp(float y) {
   const float k = __builtin_rintf(y * kLog2e);
   float r = __builtin_fmaf(-k, kLn2Hi, y);
   r = __builtin_fmaf(-k, kLn2Lo, r);
-  float q = 1.0f / 720.0f;
+  float q = 1.0f / 5040.0f;
+  q = __builtin_fmaf(q, r, 1.0f / 720.0f);
   q = __builtin_fmaf(q, r, 1.0f / 120.0f);
   q = __builtin_fmaf(q, r, 1.0f / 24.0f);
   q = __builtin_fmaf(q, r, 1.0f / 6.0f);
@@ -259,7 +261,11 @@ __device__ __forceinline__ void softmax_pool_cols(const float (&x)[NC][K], const
 #pragma unroll
   for (int k = 0; k < K; ++k)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) q[c][k] = __builtin_fmaf(1.0f / 720.0f, y[c][k], 1.0f / 120.0f);
+    for (int c = 0; c < NC; ++c) q[c][k] = __builtin_fmaf(1.0f / 5040.0f, y[c][k], 1.0f / 720.0f);
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) q[c][k] = __builtin_fmaf(q[c][k], y[c][k], 1.0f / 120.0f);
 #pragma unroll
   for (int k = 0; k < K; ++k)
 #pragma unroll
@@ -711,19 +717,22 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
 
 // Zero a byte range [begin, end) of a buffer with 16-byte stores when both
 // ends are 16-byte aligned, 4-byte stores when both are 4-byte aligned,
-// 2-byte stores otherwise (rows of an odd coff * head_dim).
+// 2-byte stores otherwise (rows of an odd coff * head_dim).  The walk steps
+// an element index (walk_elements), so a range that ends near 2^32 bytes
+// cannot wrap back onto the start of the buffer.
 __device__ __forceinline__ void zero_range(rsrc_t r, uint32_t begin, uint32_t end, uint32_t first,
                                            uint32_t step) {
   if (((begin | end) & 15u) == 0) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    for (uint32_t o = begin + first * 16u; o < end; o += step * 16u)
-      __builtin_amdgcn_raw_buffer_store_b128(z, r, o, 0, 0);
+    walk_elements<16>(begin, end, first, step,
+                      [&](uint32_t o) { __builtin_amdgcn_raw_buffer_store_b128(z, r, o, 0, 0); });
   } else if (((begin | end) & 3u) == 0) {
-    for (uint32_t o = begin + first * 4u; o < end; o += step * 4u)
-      __builtin_amdgcn_raw_buffer_store_b32(0u, r, o, 0, 0);
+    walk_elements<4>(begin, end, first, step,
+                     [&](uint32_t o) { __builtin_amdgcn_raw_buffer_store_b32(0u, r, o, 0, 0); });
   } else {
-    for (uint32_t o = begin + first * 2u; o < end; o += step * 2u)
+    walk_elements<2>(begin, end, first, step, [&](uint32_t o) {
       __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(0), r, o, 0, 0);
+    });
   }
 }
 

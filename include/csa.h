@@ -33,13 +33,18 @@
  *   (window order);  R = 1/Z (correctly rounded);  acc = fma chain of e*v
  *   from 0;  o = acc*R;  out = bf16_rne(o);  backward: G = R*f32(dout),
  *   a = e*G, dkv = bf16_rne(a), ds = a*(v - o), dscore = bf16_rne(ds).
- *   Windows longer than 64 entries (ratio 128) sum Z and acc per chunk of 64
- *   consecutive entries as above and then add the chunk sums in chunk order
- *   ([PR5984: ratio=128 commit]: per-chunk partials merged in one fixed
- *   order).
- *   EXP(y) = ldexp(P6(r), k) with y clamped to >= -104, k = rint(y*log2 e),
- *   r = y - k*ln2 in two fma steps, P6 the degree-6 Taylor polynomial of
- *   e^r (coefficients fp32(1/n!)); IEEE subnormals are kept.
+ *   At ratio 2 and 4 the kernels evaluate exactly this order.  At ratio 128
+ *   (windows of 128 or 256 entries) they sum Z and acc per chunk of 64
+ *   consecutive entries in this order and then add the chunk sums in chunk
+ *   order ([PR5984: ratio=128 commit]: per-chunk partials merged in one fixed
+ *   order), which is still fixed (bit-identical run to run) but differs from
+ *   the single chain above by the rounding of the reordered sums: out, dkv
+ *   within one bf16 ulp of the single-chain result or the error bound of the
+ *   reordering, dscore likewise, dape within 1e-5 of its largest magnitude.
+ *   EXP(y) = ldexp(P7(r), k) with y clamped to >= -104, k = rint(y*log2 e),
+ *   r = y - k*ln2 in two fma steps, P7 the degree-7 Taylor polynomial of
+ *   e^r (coefficients fp32(1/n!)), within 1 fp32 ulp of e^y over [-104, 0];
+ *   IEEE subnormals are kept.
  *
  * Conventions for every entry point:
  *   - All device pointers are caller-owned; libcsa never allocates, frees or

@@ -118,7 +118,7 @@ def exp_f32_array(y) -> np.ndarray:
 
 
 def exp_constants() -> np.ndarray:
-    out = np.zeros(11, np.float32)
+    out = np.zeros(12, np.float32)
     lib().oracle_exp_constants(_ptr(out))
     return out
 

@@ -46,14 +46,12 @@
  *             Z   = ((e_0 + e_1) + e_2) + ...              (window order)
  *             R   = 1 / Z                                  (correctly rounded)
  *             acc = fma(e_{K-1}, v_{K-1}, ... fma(e_0, v_0, 0))
- *           Windows longer than SUM_CHUNK = 64 entries (ratio 128) sum in
- *           chunks of 64 consecutive entries instead: each chunk's Z and acc
- *           as above over its own entries, then the chunk sums added in
- *           chunk order, Z = ((Z_0 + Z_1) + Z_2) + ..., acc likewise
- *           ([PR5984: ratio=128 commit] merges per-chunk partials in one
- *           fixed order; the window max is taken over the whole window
- *           first, so no rescaling is needed).  Windows of at most 64
- *           entries are one chunk: the rule above.
+ *           Every window, of any length (ratio 128 gives 128 or 256
+ *           entries), is summed this way in one chain: the pages fix fp32
+ *           intermediates but no chunking, so the plain single-chain order is
+ *           the reference.  A kernel that sums in chunks and merges the
+ *           chunk sums ([PR5984: ratio=128 commit]) is compared with it
+ *           within the rounding such a reordering can cause, not bit for bit.
  *             o   = acc * R,  out = bf16_rne(o)
  *             G   = R * f32(dOut),  a_k = e_k * G
  *             dKV_k = bf16_rne(a_k),  ds_k = a_k * (v_k - o),
@@ -64,7 +62,7 @@
  *                                      smallest fp32 subnormal)
  *             k  = rint(y * L2E)
  *             r  = fma(-k, LN2_LO, fma(-k, LN2_HI, y))     (Cody-Waite)
- *             q  = Taylor polynomial of e^r, degree 6, Horner with fma,
+ *             q  = Taylor polynomial of e^r, degree 7, Horner with fma,
  *                  coefficients fp32(1/n!)
  *             EXP = ldexp(q, k)
  *   Built with -ffp-contract=off: every fma above is explicit, nothing else
@@ -120,9 +118,9 @@ uint16_t oracle_bf16_from_f32(float f)
 static const float L2E = 0x1.715476p+0f;     /* fp32 nearest to log2(e)        */
 static const float LN2_HI = 0x1.62e430p-1f;  /* fp32 nearest to ln(2)          */
 static const float LN2_LO = -0x1.05c610p-29f;/* fp32 nearest to ln(2) - LN2_HI */
-static const float EXP_C[7] = {              /* fp32 nearest to 1/n!, n=0..6   */
+static const float EXP_C[8] = {              /* fp32 nearest to 1/n!, n=0..7   */
     0x1.000000p+0f, 0x1.000000p+0f, 0x1.000000p-1f, 0x1.555556p-3f,
-    0x1.555556p-5f, 0x1.111112p-7f, 0x1.6c16c2p-10f};
+    0x1.555556p-5f, 0x1.111112p-7f, 0x1.6c16c2p-10f, 0x1.a01a02p-13f};
 static const float EXP_Y_MIN = -104.0f;
 
 float oracle_exp_f32(float y)
@@ -132,8 +130,8 @@ float oracle_exp_f32(float y)
     float k = rintf(t);
     float r = fmaf(-k, LN2_HI, y);
     r = fmaf(-k, LN2_LO, r);
-    float q = EXP_C[6];
-    for (int n = 5; n >= 0; --n) q = fmaf(q, r, EXP_C[n]);
+    float q = EXP_C[7];
+    for (int n = 6; n >= 0; --n) q = fmaf(q, r, EXP_C[n]);
     return ldexpf(q, (int)k);
 }
 
@@ -146,14 +144,14 @@ void oracle_exp_f32_array(const float* y, float* out, int64_t n)
 
 /* Expose the constants so the pin tests can check them against their exact
  * definitions.  out[0]=L2E, out[1]=LN2_HI, out[2]=LN2_LO, out[3]=y_min,
- * out[4..10]=EXP_C[0..6]. */
+ * out[4..11]=EXP_C[0..7]. */
 void oracle_exp_constants(float* out)
 {
     out[0] = L2E;
     out[1] = LN2_HI;
     out[2] = LN2_LO;
     out[3] = EXP_Y_MIN;
-    for (int n = 0; n < 7; ++n) out[4 + n] = EXP_C[n];
+    for (int n = 0; n < 8; ++n) out[4 + n] = EXP_C[n];
 }
 
 /* OpenMP threads used by the parallel window loops (reported with timings). */
@@ -256,9 +254,6 @@ static void free_blocks(blocks_t* bl)
 /* fp32 oracle (fixed evaluation order, see header)                        */
 /* ---------------------------------------------------------------------- */
 
-/* Window entries per summation chunk (see the header). */
-#define SUM_CHUNK 64
-
 /* Shared body of the fp32 forward and backward: one (block, column) window.
  * Fills e[], v[], returns R and o. */
 static void window_f32(const uint16_t* kv, const uint16_t* score,
@@ -275,16 +270,10 @@ static void window_f32(const uint16_t* kv, const uint16_t* score,
     float m = x[0];
     for (int k = 1; k < K; ++k) m = fmaxf(m, x[k]);
     for (int k = 0; k < K; ++k) e[k] = oracle_exp_f32(x[k] - m);
-    float Z = 0.0f, acc = 0.0f;
-    for (int c0 = 0; c0 < K; c0 += SUM_CHUNK) {
-        const int c1 = (c0 + SUM_CHUNK < K) ? c0 + SUM_CHUNK : K;
-        float zc = e[c0];
-        for (int k = c0 + 1; k < c1; ++k) zc = zc + e[k];
-        float ac = 0.0f;
-        for (int k = c0; k < c1; ++k) ac = fmaf(e[k], v[k], ac);
-        Z = (c0 == 0) ? zc : Z + zc;
-        acc = (c0 == 0) ? ac : acc + ac;
-    }
+    float Z = e[0];
+    for (int k = 1; k < K; ++k) Z = Z + e[k];
+    float acc = 0.0f;
+    for (int k = 0; k < K; ++k) acc = fmaf(e[k], v[k], acc);
     float R = 1.0f / Z;
     *R_out = R;
     *o_out = acc * R;

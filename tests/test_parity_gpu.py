@@ -1,9 +1,13 @@
 """GPU parity: libcsa (HIP, through the C ABI) against the CPU oracle.
 
 Contract (checked element by element on seeded inputs):
-  * out, dKV, dScore: bit-identical to the oracle's fp32 evaluation order
-    (the stated tolerance is 1 bf16 ulp; both sides evaluate the same fixed
-    fp32 order, so the expected difference is none);
+  * ratio 2 and 4: out, dKV, dScore bit-identical to the oracle's fp32
+    evaluation order (the stated tolerance is 1 bf16 ulp; both sides evaluate
+    the same fixed fp32 order, so the expected difference is none);
+  * ratio 128: the kernels sum each window in 64-entry chunks, the oracle in
+    one chain, so results are compared within 1 bf16 ulp or the error bound
+    of that reordering, with the pages' ratio-128 gate as a floor
+    (tests/tolerance.py);
   * never-consumed dKV/dScore slots: exactly 0x0000 although the output
     buffers were filled with NaN before the call;
   * dAPE: |gpu - ref| <= 1e-5 * max(|ref|, max|ref|) with ref the double sum
@@ -20,6 +24,7 @@ import gated_pooling_amd as G
 import oracle
 from gated_pooling_amd import inputs
 from tests import brute
+from tests.tolerance import check_reordered
 
 pytestmark = pytest.mark.gpu
 
@@ -90,13 +95,17 @@ def assert_dape(got, ref):
     assert np.all(err <= tol), f"dAPE max err {err.max():.3e}, max rel-to-scale {(err / scale).max():.3e}"
 
 
-def check_against_oracle(cu, T, r, c, d, kv, sc, ape, dout, got):
+def check_against_oracle(cu, T, r, c, d, kv, sc, ape, dout, got, label=""):
     N = oracle.total_comp(cu, r)
     kvb, scb, apen, doutb = inputs.bits(kv), inputs.bits(sc), ape.numpy(), inputs.bits(dout)
     out_ref = oracle.fwd_f32(kvb, scb, apen, cu, T, r, c, d)
     dkv_ref, dsc_ref, dape_ref, _, _ = oracle.bwd_f32(kvb, scb, apen, cu, T, r, c, d, doutb)
     out, dkv, dsc, dape = got
     assert out.shape == (N, d)
+    if r == 128:
+        unused = ~brute.consumed_mask(cu, T, r, c, d)
+        check_reordered(cu, T, r, c, d, kvb, got, (out_ref, dkv_ref, dsc_ref, dape_ref), unused, label=label)
+        return out_ref, dkv_ref, dsc_ref, dape_ref
     assert_bits_equal(out, out_ref, "out")
     assert_bits_equal(dkv, dkv_ref, "dkv")
     assert_bits_equal(dsc, dsc_ref, "dscore")
@@ -120,7 +129,7 @@ def test_workload_parity(dev, name, host):
     assert N == oracle.total_comp(cu, r)
     kv, sc, ape, dout = inputs.make_tensors(wl, N)
     got = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N, host=host)
-    check_against_oracle(cu, T, r, c, d, kv, sc, ape, dout, got)
+    check_against_oracle(cu, T, r, c, d, kv, sc, ape, dout, got, label=f"{name}/{'args' if host else 'device'}")
 
 
 def test_stage_split_equals_full_backward(dev):
@@ -143,7 +152,7 @@ def test_repeat_runs_bit_identical(dev, name):
     N = G.csa_compressor_total_comp(cu, r)
     kv, sc, ape, dout = inputs.make_tensors(wl, N)
     first = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N)
-    for _ in range(4):
+    for _ in range(10):
         again = run_gpu(dev, cu, T, r, c, d, kv, sc, ape, dout, N)
         for x, y in zip(first, again):
             assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
@@ -296,16 +305,17 @@ def _r128_cases():
 
 @pytest.mark.parametrize("case", _r128_cases(), ids=lambda c: f"S{len(c[0])}_c{c[2]}_d{c[3]}_s{c[4]}")
 def test_ratio128_packs(dev, case):
-    """ratio 128: windows of 128 * coff rows staged through LDS, chunked
-    sums; multi-block segments, tails, segments shorter than 128, padding,
-    kernel-argument / LDS / workspace segment tables."""
+    """ratio 128: windows of 128 * coff rows staged through LDS, summed in
+    64-entry chunks (compared within the reordering tolerance); multi-block
+    segments, tails, segments shorter than 128, padding, kernel-argument /
+    LDS / workspace segment tables."""
     lengths, T, c, d, seed, host = case
     wl = inputs.custom("r128", lengths, T, 128, c, d, seed=seed)
     cu = list(wl.cu_seqlens)
     N = G.csa_compressor_total_comp(cu, 128)
     kv, sc, ape, dout = inputs.make_tensors(wl, N)
     got = run_gpu(dev, cu, T, 128, c, d, kv, sc, ape, dout, N, host=host)
-    check_against_oracle(cu, T, 128, c, d, kv, sc, ape, dout, got)
+    check_against_oracle(cu, T, 128, c, d, kv, sc, ape, dout, got, label=f"r128pack_s{seed}")
 
 
 def test_extreme_scores_and_subnormals(dev):

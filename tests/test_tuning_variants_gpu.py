@@ -30,6 +30,7 @@ VARIANTS = [
     {"CSA_FWD_MAX_WGS": "37", "CSA_BWD_MAX_WGS": "6", "CSA_FWD_PREFETCH": "4"},
     {"CSA_BWD_SLICE_BYTES": "256", "CSA_BWD_MAX_WGS": "1000"},
     {"CSA_BWD_SLICE_BYTES": "2048"},
+    {"CSA_BWD_SLICE_BYTES": "384"},   # not a power of two: rounded down to 256-byte slices
 ]
 
 # ratio-128 grid caps: fewer workgroups than column slices (one per slice),
