@@ -1,13 +1,20 @@
 """Build libcsa.so (the HIP library) in-tree for gfx950.
 
     python -m gated_pooling_amd.build
+    python -m gated_pooling_amd.build --resources OUT.md   # per-kernel resource report
 
 Flags: -ffp-contract=off so only explicit fmas are fused (the fp32
 evaluation order is fixed); packed fp32 instructions are disabled.
+
+--resources compiles the kernels once more for the device only with the
+compiler's kernel-resource-usage remarks and writes, for every kernel
+instance, its VGPRs, AGPRs, SGPRs, scratch, spills, static LDS and the
+occupancy the compiler derives from them (waves per SIMD).
 """
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 
@@ -45,5 +52,53 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     return LIB
 
 
+def resource_usage(extra_flags=None):
+    """{demangled kernel name: {field: value}} from the compiler's
+    kernel-resource-usage remarks on the device code of csa_kernels.hip."""
+    import tempfile
+    with tempfile.TemporaryDirectory() as tmp:
+        cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared", "-fPIC")], *(extra_flags or []), "--cuda-device-only",
+               "-c", "-Rpass-analysis=kernel-resource-usage", "-o", os.path.join(tmp, "k.o"), SOURCES[0]]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr[-4000:]}")
+    kernels, cur = {}, None
+    for line in res.stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = kernels.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+(?:\[[^\]]*\])?): (\S+) \[-Rpass", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = m.group(2)
+    names = list(kernels)
+    import shutil
+    filt = shutil.which("c++filt") or shutil.which("llvm-cxxfilt")
+    dem = subprocess.run([filt], input="\n".join(names), capture_output=True, text=True).stdout.splitlines() \
+        if filt else names
+    return {(dem[i] if i < len(dem) else n): kernels[n] for i, n in enumerate(names)}
+
+
+def write_resource_report(path, extra_flags=None):
+    rows = resource_usage(extra_flags)
+    cols = ["VGPRs", "AGPRs", "TotalSGPRs", "ScratchSize [bytes/lane]", "VGPRs Spill", "SGPRs Spill",
+            "LDS Size [bytes/block]", "Occupancy [waves/SIMD]"]
+    with open(path, "w") as f:
+        f.write("| kernel instance | " + " | ".join(cols) + " |\n|" + "---|" * (len(cols) + 1) + "\n")
+        for name in sorted(rows):
+            short = name.replace("csa::(anonymous namespace)::", "")
+            short = short[short.find(" ") + 1:] if short.startswith("void ") else short
+            short = re.sub(r"\(.*\)$", "", short)
+            f.write(f"| `{short}` | " + " | ".join(rows[name].get(c, "") for c in cols) + " |\n")
+    return path
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--resources", metavar="OUT.md", help="write the per-kernel resource report and exit")
+    a = ap.parse_args()
+    if a.resources:
+        print(write_resource_report(a.resources))
+    else:
+        print(build(verbose=True))
