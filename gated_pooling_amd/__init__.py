@@ -10,8 +10,8 @@ Low level (same names and arguments as ``include/csa.h``, raw pointers):
   csa_compressor_total_comp, csa_compressor_check_support,
   csa_compressor_fwd_workspace_size, csa_compressor_bwd_workspace_size,
   csa_compressor_fwd, csa_compressor_bwd, csa_compressor_bwd_grads,
-  csa_compressor_bwd_dape_reduce, csa_status_string, csa_last_error,
-  csa_version
+  csa_compressor_bwd_dape_reduce, csa_compressor_bwd_noalloc,
+  csa_status_string, csa_last_error, csa_version
 
 Tensor level:
   compressor_fwd(kv, score, ape, cu_seqlens, ratio, coff, total_comp, ...) -> out
@@ -83,6 +83,8 @@ def lib():
         L.csa_compressor_bwd_grads.argtypes = [P, P, P, P, P, i32, i64, i64, i32, i32, i32, P, P, P, P, sz, P]
         L.csa_compressor_bwd_dape_reduce.restype = st
         L.csa_compressor_bwd_dape_reduce.argtypes = [i32, i32, i32, i32, i64, i64, P, P, sz, P]
+        L.csa_compressor_bwd_noalloc.restype = st
+        L.csa_compressor_bwd_noalloc.argtypes = [P, P, P, P, P, i32, i64, i64, i32, i32, i32, P, P, P, P, i32, P]
         _lib = L
     return _lib
 
@@ -173,6 +175,13 @@ def csa_compressor_bwd_dape_reduce(ratio, coff, head_dim, num_segments, total_to
     _check(lib().csa_compressor_bwd_dape_reduce(ratio, coff, head_dim, num_segments, total_tokens, total_comp, dape,
                                                 workspace, workspace_bytes, stream),
            "csa_compressor_bwd_dape_reduce")
+
+
+def csa_compressor_bwd_noalloc(kv, score, ape, cu_seqlens, cu_seqlens_host, num_segments, total_tokens, total_comp,
+                               ratio, coff, head_dim, dout, dkv, dscore, dape, deterministic, stream) -> None:
+    _check(lib().csa_compressor_bwd_noalloc(kv, score, ape, cu_seqlens, cu_seqlens_host, num_segments, total_tokens,
+                                            total_comp, ratio, coff, head_dim, dout, dkv, dscore, dape,
+                                            deterministic, stream), "csa_compressor_bwd_noalloc")
 
 
 # ---------------------------------------------------------------------------

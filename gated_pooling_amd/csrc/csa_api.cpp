@@ -428,10 +428,9 @@ csa_status_t launch_scan_if_needed(const Problem& p, const Plan& pl, const int32
   return after_launch("segment scan");
 }
 
-// Validation shared by the backward entry points.
-csa_status_t check_bwd_args(const Problem& pr, const Plan& pl, const void* kv, const void* score,
-                            const float* ape, const int32_t* cu, const void* dout, const void* dkv,
-                            const void* dscore, const void* workspace, size_t workspace_bytes) {
+// Validation of the backward's tensors (shared by the backward entry points).
+csa_status_t check_bwd_io(const Problem& pr, const void* kv, const void* score, const float* ape,
+                          const int32_t* cu, const void* dout, const void* dkv, const void* dscore) {
   csa_status_t st;
   if (pr.T > 0) {
     if ((st = check_ptr(dkv, "dkv")) || (st = check_ptr(dscore, "dscore"))) return st;
@@ -444,6 +443,15 @@ csa_status_t check_bwd_args(const Problem& pr, const Plan& pl, const void* kv, c
   // the backward always launches (it must zero its outputs), so cu is read
   if (!cu) return fail(CSA_STATUS_INVALID_VALUE, "cu_seqlens is null");
   if (reinterpret_cast<uintptr_t>(cu) & 3u) return fail(CSA_STATUS_INVALID_VALUE, "cu_seqlens is not 4-byte aligned");
+  return CSA_STATUS_SUCCESS;
+}
+
+// Validation shared by the backward entry points with a caller workspace.
+csa_status_t check_bwd_args(const Problem& pr, const Plan& pl, const void* kv, const void* score,
+                            const float* ape, const int32_t* cu, const void* dout, const void* dkv,
+                            const void* dscore, const void* workspace, size_t workspace_bytes) {
+  csa_status_t st;
+  if ((st = check_bwd_io(pr, kv, score, ape, cu, dout, dkv, dscore))) return st;
   if (workspace_bytes < pl.ws_bwd)
     return fail(CSA_STATUS_WORKSPACE_TOO_SMALL, "backward needs %llu workspace bytes, got %llu",
                 (unsigned long long)pl.ws_bwd, (unsigned long long)workspace_bytes);
@@ -664,6 +672,32 @@ csa_status_t csa_compressor_bwd(const void* kv, const void* score, const float* 
   if ((st = check_ptr(dape, "dape"))) return st;
   if ((st = launch_bwd_grads(pr, pl, kv, score, ape, cu, cu_host, dout, dkv, dscore, workspace, stream))) return st;
   return launch_reduce(pr, pl, dape, workspace, stream);
+}
+
+csa_status_t csa_compressor_bwd_noalloc(const void* kv, const void* score, const float* ape, const int32_t* cu,
+                                        const int32_t* cu_host, int32_t S, int64_t total_tokens,
+                                        int64_t total_comp, int32_t ratio, int32_t coff, int32_t head_dim,
+                                        const void* dout, void* dkv, void* dscore, float* dape,
+                                        int32_t deterministic, hipStream_t stream) {
+  (void)deterministic;  // dAPE is always reduced in a fixed order
+  const Problem pr{ratio, coff, head_dim, S, total_tokens, total_comp};
+  csa_status_t st = check_problem(pr);
+  if (st) return st;
+  if ((st = check_host_cu(pr, cu_host))) return st;
+  const Plan pl = make_plan(pr);
+  if (pl.ws_bwd > csa::kNoAllocScratchBytes)
+    return fail(CSA_STATUS_WORKSPACE_TOO_SMALL,
+                "this problem needs %llu bytes of scratch; the allocation-free backward holds %llu per GPU "
+                "(use csa_compressor_bwd with a workspace)",
+                (unsigned long long)pl.ws_bwd, (unsigned long long)csa::kNoAllocScratchBytes);
+  if ((st = check_bwd_io(pr, kv, score, ape, cu, dout, dkv, dscore))) return st;
+  if ((st = check_ptr(dape, "dape"))) return st;
+  void* ws = nullptr;
+  const hipError_t e = csa::noalloc_scratch(&ws);
+  if (e != hipSuccess)
+    return fail(CSA_STATUS_DEVICE_ERROR, "library scratch of the current device not found: %s", hipGetErrorString(e));
+  if ((st = launch_bwd_grads(pr, pl, kv, score, ape, cu, cu_host, dout, dkv, dscore, ws, stream))) return st;
+  return launch_reduce(pr, pl, dape, ws, stream);
 }
 
 }  // extern "C"

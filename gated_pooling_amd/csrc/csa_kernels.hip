@@ -48,6 +48,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "csa_launch.h"
@@ -1739,6 +1740,40 @@ bool launch_seg_scan(int ratio, const SegParams& sp, int32_t* off, int32_t* flag
     return true;
   }
   return false;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch owned by the library, for the backward entry point that allocates
+// nothing (csa_compressor_bwd_noalloc): the workspace of the ordinary entry
+// point (validity flag, segment table, dAPE partials) lives here instead.
+// Each GPU the library runs on holds its own copy from the module's load
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: kernels receive the address that hipGetSymbolAddress
+// returns for the current device, looked up once per device and cached.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace csa

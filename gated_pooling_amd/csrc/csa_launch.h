@@ -134,4 +134,9 @@ bool launch_seg_scan(int ratio, const SegParams& sp, int32_t* off, int32_t* flag
 bool launch_fwd128(int coff, const Fwd128Params& p, uint32_t grid, size_t lds_bytes, hipStream_t st);
 bool launch_bwd128(int coff, const Bwd128Params& p, uint32_t grid, size_t lds_bytes, hipStream_t st);
 
+// Library-owned device scratch of the allocation-free backward: its size and
+// the address of the current device's copy (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t{40} << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace csa

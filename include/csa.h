@@ -205,6 +205,33 @@ csa_status_t csa_compressor_bwd_dape_reduce(int32_t ratio, int32_t coff, int32_t
                                             void* workspace, size_t workspace_bytes,
                                             hipStream_t stream);
 
+/* The backward (same arguments, same results, bit for bit, as
+ * csa_compressor_bwd) without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It calls no allocating routine; the
+ * workspace lives in scratch memory owned by the library: one array of
+ * CSA_NOALLOC_SCRATCH_BYTES per GPU, held from the library's load on that
+ * GPU until the process ends, its address looked up on the first call on
+ * each device (the device current at the call is used).
+ *   - A problem whose workspace (csa_compressor_bwd_workspace_size) exceeds
+ *     CSA_NOALLOC_SCRATCH_BYTES is rejected with
+ *     CSA_STATUS_WORKSPACE_TOO_SMALL before anything is enqueued; every
+ *     ratio 2 / 4 problem of the envelope fits at the default launch shapes,
+ *     ratio 128 up to about 32 MiB of dAPE partials.
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents; nothing in it has to start at zero.  Calls that
+ *     overlap on one GPU (different streams, or different host threads,
+ *     without ordering between them) race on it and give undefined results.
+ *   - CSA_STATUS_DEVICE_ERROR if the scratch of the current device cannot be
+ *     located. */
+#define CSA_NOALLOC_SCRATCH_BYTES (40u * 1024u * 1024u)
+csa_status_t csa_compressor_bwd_noalloc(const void* kv, const void* score, const float* ape,
+                                        const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                        int32_t num_segments, int64_t total_tokens, int64_t total_comp,
+                                        int32_t ratio, int32_t coff, int32_t head_dim,
+                                        const void* dout, void* dkv, void* dscore, float* dape,
+                                        int32_t deterministic, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -201,6 +201,25 @@ def test_bwd_rejections_happen_before_any_launch():
     assert L.csa_compressor_bwd_dape_reduce(3, 2, 16, 2, 64, 15, A, A, need, NULL) == NS
 
 
+def test_noalloc_rejections_happen_before_any_device_call():
+    """The allocation-free backward validates the problem, its scratch need
+    and every caller pointer on the host before it looks up the device."""
+    INV, NS, WS = G.CSA_STATUS_INVALID_VALUE, G.CSA_STATUS_NOT_SUPPORTED, G.CSA_STATUS_WORKSPACE_TOO_SMALL
+    L = G.lib()
+
+    def call(kv=A, dkv=A, dsc=A, dape=A, dout=A, cu=B, r=4, S=2, T=64, N=15, d=16):
+        return L.csa_compressor_bwd_noalloc(kv, kv, kv, cu, NULL, S, T, N, r, 2, d, dout, dkv, dsc, dape, 1, NULL)
+
+    assert call(r=5) == NS
+    assert call(dkv=NULL) == INV
+    assert call(dape=NULL) == INV
+    assert call(dout=MISALIGNED) == INV
+    assert call(cu=NULL) == INV
+    # ten million segments: the segment table alone exceeds the library's scratch
+    assert call(S=10_000_000, T=65536, N=512, r=128, d=64) == WS
+    assert "scratch" in G.csa_last_error()
+
+
 def test_host_cu_is_validated_before_any_launch():
     INV = G.CSA_STATUS_INVALID_VALUE
     bad_total = G.host_cu([0, 37, 60])      # 9 + 5 = 14 rows, not 15
