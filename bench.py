@@ -13,12 +13,18 @@ forwards of a group of sets and then their backwards (as a training step
 does layer by layer); every kernel therefore reads inputs that at least
 ~400 MB of other traffic has passed through since they were last touched.
 
+Order: the context legs (a 512 MiB device copy, the warm-cache kernel times,
+hipGraph replays, the fp32 PyTorch eager comparison) run first; they also
+bring the GPU clocks from idle to their loaded state, which takes ~10 ms.
+Then W warm-up steps and the timed region of K steps.
+
 Prints ONE JSON line: value = algorithmic HBM bytes of the step / time per
 step (GB/s), from a timed region of K steps with nothing inside but the
-work.  A second timed region repeats the K steps with HIP events recorded on
-the launch stream around every kernel; the per-kernel averages and the
-roofline object (for the dominant kernel) come from it.  The CPU oracle is
-timed on the host as a baseline.
+work.  Further timed regions repeat the K steps with the segment table read
+from the device copy of cu_seqlens (no host copy), and with HIP events
+recorded on the launch stream around every kernel; the
+per-kernel averages and the roofline object (for the dominant kernel) come
+from the last.  The CPU oracle is timed on the host as a baseline.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--sets S]
 """
@@ -311,27 +317,30 @@ def main():
     L = G.lib()
     cu_host = G.host_cu(cu)  # host copy: small packs get the segment table as kernel arguments
 
-    def fwd(st):
+    def fwd(st, host=None):
         p = st["p"]
-        rc = L.csa_compressor_fwd(p["kv"], p["sc"], p["ape"], p["cu"], cu_host, S, T, N, r, c, d, p["out"],
-                                  p["fws"], st["fws"].numel(), cur["s"])
+        rc = L.csa_compressor_fwd(p["kv"], p["sc"], p["ape"], p["cu"], cu_host if host is None else host, S, T, N,
+                                  r, c, d, p["out"], p["fws"], st["fws"].numel(), cur["s"])
         assert rc == 0, G.csa_last_error()
 
-    def grads(st):
+    def grads(st, host=None):
         p = st["p"]
-        rc = L.csa_compressor_bwd_grads(p["kv"], p["sc"], p["ape"], p["cu"], cu_host, S, T, N, r, c, d, p["dout"],
-                                        p["dkv"], p["dsc"], p["bws"], st["bws"].numel(), cur["s"])
+        rc = L.csa_compressor_bwd_grads(p["kv"], p["sc"], p["ape"], p["cu"], cu_host if host is None else host, S, T,
+                                        N, r, c, d, p["dout"], p["dkv"], p["dsc"], p["bws"], st["bws"].numel(),
+                                        cur["s"])
         assert rc == 0, G.csa_last_error()
 
-    def reduce(st):
+    def reduce(st, s=None):
         p = st["p"]
-        rc = L.csa_compressor_bwd_dape_reduce(r, c, d, S, T, N, p["dape"], p["bws"], st["bws"].numel(), cur["s"])
+        rc = L.csa_compressor_bwd_dape_reduce(r, c, d, S, T, N, p["dape"], p["bws"], st["bws"].numel(),
+                                              cur["s"] if s is None else s)
         assert rc == 0, G.csa_last_error()
 
     nsets = len(sets)
 
     def run_steps(K):
-        """K steps in groups of nsets: the group's forwards, then its backwards."""
+        """K steps on one stream, in groups of nsets: the group's forwards,
+        then its backwards (gradients, dAPE reduce)."""
         done = 0
         while done < K:
             grp = list(range(min(nsets, K - done)))
@@ -341,6 +350,19 @@ def main():
                 grads(sets[j])
                 reduce(sets[j])
             done += len(grp)
+
+    def timed_steps(K, runner):
+        """Wall time per step and event time per step of K steps, bracketed
+        by a device synchronization on both sides."""
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        runner(K)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall * 1e3 / K, ev[0].elapsed_time(ev[1]) / K
 
     def run_steps_timed(K):
         """The same K steps with each kernel's launches of a group issued back
@@ -361,22 +383,109 @@ def main():
             done += len(grp)
         return spans
 
-    # warm-up, then the timed region: K steps, nothing but the work itself
-    run_steps(max(args.warmup, 0))
-    torch.cuda.synchronize()
+    # ---- context legs first: they also bring the GPU's clocks from idle to
+    # their loaded state before the timed steps (the step time swings by up to
+    # 25 % during the first ~10 ms of load after idling) ----
+    t_ctx = time.perf_counter()
     K = args.steps
-    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    region[0].record(stream)
-    run_steps(K)
-    region[1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / K
-    gpu_ms_per_step = region[0].elapsed_time(region[1]) / K
 
-    # second timed region: the same K steps, per-kernel HIP events
+    # a plain device-to-device copy of 512 MiB (torch's copy kernel)
+    src = torch.empty(256 * 2 ** 20, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 2 * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+
+    warm = None
+    if not args.no_warm:  # one buffer set over and over (inputs cache-resident)
+        warm = {}
+        for name, fn in (("fwd", fwd), ("bwd_grads", grads), ("dape_reduce", reduce)):
+            for _ in range(3):
+                fn(sets[0])
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ea.record(stream)
+            for _ in range(20):
+                fn(sets[0])
+            eb.record(stream)
+            torch.cuda.synchronize()
+            warm[name] = round(ea.elapsed_time(eb) * 1e3 / 20, 3)
+
+    graph = None
+    if not args.no_graph:
+        # the same launches captured once into hipGraphs and replayed: a
+        # forward-only graph and a forward + backward graph (one stream) over
+        # the buffer sets
+        def captured(fn):
+            g = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cap):
+                cur["s"] = ctypes.c_void_p(cap.cuda_stream)
+                fn()  # warm-up on the side stream, as torch's capture pattern asks
+            torch.cuda.current_stream().wait_stream(cap)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                cur["s"] = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+                fn()
+            cur["s"] = sptr
+            torch.cuda.synchronize()
+            return g
+
+        def replay_us(g, reps):
+            for _ in range(5):
+                g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / (reps * nsets)
+
+        g_fwd = captured(lambda: [fwd(st) for st in sets])
+        g_step = captured(lambda: run_steps(nsets))
+        reps = max(40, K // nsets)
+        graph = {"fwd_us": round(replay_us(g_fwd, reps), 3), "fwd_bwd_us": round(replay_us(g_step, reps), 3),
+                 "replays": reps}
+        del g_fwd, g_step
+
+    eager = None
+    if not args.no_eager:
+        eager_us = eager_timing(wl, N, sets, stream, steps=20)
+        eager = {"fwd_bwd_us": round(eager_us, 1),
+                 "what": "PyTorch fp32 eager forward + autograd backward of the same op, same buffers"}
+    torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_ctx) * 1e3
+
+    # ---- warm-up, then the timed region: K steps, nothing but the work ----
+    run_steps(max(args.warmup, 0))
+    ms_per_step, gpu_ms_per_step = timed_steps(K, run_steps)
+
+    # the same K steps with the segment table read from the device copy of
+    # cu_seqlens (no host copy): what a graph replayed with new cu_seqlens runs
+    nohost = ctypes.c_void_p(0)
+
+    def run_steps_device_table(k):
+        done = 0
+        while done < k:
+            grp = list(range(min(nsets, k - done)))
+            for j in grp:
+                fwd(sets[j], nohost)
+            for j in grp:
+                grads(sets[j], nohost)
+                reduce(sets[j])
+            done += len(grp)
+
+    devtab_ms, _ = timed_steps(K, run_steps_device_table)
+
+    # per-kernel region: the same K steps, per-kernel HIP events
     torch.cuda.synchronize()
     spans = run_steps_timed(K)
     torch.cuda.synchronize()
@@ -394,77 +503,8 @@ def main():
     achieved = kern[dom]["GBs"]
     traffic = load_traffic(dom, wname)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-
-    warm = None
-    if not args.no_warm:  # context: one buffer set over and over (inputs cache-resident)
-        warm = {}
-        for name, fn in (("fwd", fwd), ("bwd_grads", grads), ("dape_reduce", reduce)):
-            for _ in range(3):
-                fn(sets[0])
-            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            ea.record(stream)
-            for _ in range(20):
-                fn(sets[0])
-            eb.record(stream)
-            torch.cuda.synchronize()
-            warm[name] = round(ea.elapsed_time(eb) * 1e3 / 20, 3)
-
-    # context: a plain device-to-device copy of 512 MiB (torch's copy kernel)
-    src = torch.empty(256 * 2 ** 20, dtype=torch.int16, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(5):
-        dst.copy_(src)
-    b.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * src.numel() * 2 * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
-    del src, dst
-
-    graph = None
-    if not args.no_graph:
-        # the same launches captured once into hipGraphs and replayed: a
-        # forward-only graph and a forward + backward graph over the buffer sets
-        def captured(fn):
-            g = torch.cuda.CUDAGraph()
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                cur["s"] = ctypes.c_void_p(side.cuda_stream)
-                fn()  # warm-up on the side stream, as torch's capture pattern asks
-            torch.cuda.current_stream().wait_stream(side)
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g):
-                cur["s"] = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-                fn()
-            cur["s"] = sptr
-            torch.cuda.synchronize()
-            return g
-
-        def replay_us(g, reps):
-            for _ in range(3):
-                g.replay()
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(reps):
-                g.replay()
-            b.record(stream)
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) * 1e3 / (reps * nsets)
-
-        g_fwd = captured(lambda: [fwd(st) for st in sets])
-        g_step = captured(lambda: run_steps(nsets))
-        reps = max(1, K // nsets)
-        graph = {"fwd_us": round(replay_us(g_fwd, reps), 3), "fwd_bwd_us": round(replay_us(g_step, reps), 3)}
-        del g_fwd, g_step
-
-    eager = None
-    if not args.no_eager:
-        eager_us = eager_timing(wl, N, sets, stream, steps=20)
-        eager = {"fwd_bwd_us": round(eager_us, 1), "speedup": round(eager_us / (ms_per_step * 1e3), 1),
-                 "what": "PyTorch fp32 eager forward + autograd backward of the same op, same buffers"}
+    if eager is not None:
+        eager["speedup"] = round(eager["fwd_bwd_us"] / (ms_per_step * 1e3), 1)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -493,7 +533,8 @@ def main():
                    "total_tokens": T, "total_comp": N, "ratio": r, "coff": c, "head_dim": d,
                    "cache": f"cold ({nsets} rotating buffer sets)"},
         "us_per_call": {"fwd": fwd_us, "bwd": round(bwd_us, 3), "fwd_bwd": round(fwd_us + bwd_us, 3),
-                        "step_wall": round(ms_per_step * 1e3, 3), "step_gpu": round(gpu_ms_per_step * 1e3, 3)},
+                        "step_wall": round(ms_per_step * 1e3, 3), "step_gpu": round(gpu_ms_per_step * 1e3, 3),
+                        "step_device_table": round(devtab_ms * 1e3, 3)},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "step_algorithmic_bytes": step_bytes,
         "kernels": kern,
@@ -501,6 +542,8 @@ def main():
         "copy_kernel_GBs": round(copy_gbs, 1),
         "graph_us": graph,
         "eager": eager,
+        "clock_settle": {"ms": round(settle_ms, 1),
+                         "what": "the context legs above (copy, warm, graph, eager) run before the warm-up steps"},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
