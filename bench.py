@@ -253,6 +253,57 @@ def cpu_baseline(wl, N, kv, sc, ape, dout, budget_s):
     return reps, el, oracle.num_threads()
 
 
+def cpu_table(path):
+    """The CPU oracle (fp32 evaluation order) timed on every workload: forward
+    and backward separately, median of 3 after one warm-up, on all host
+    threads and on one thread.  Writes a JSON record with the CPU model."""
+    import platform
+    import statistics
+
+    import numpy as np
+
+    import oracle
+    from gated_pooling_amd import inputs
+
+    model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    full = oracle.num_threads()
+    rec = {"cpu_model": model or platform.processor(), "threads_all": full, "host_cpus": os.cpu_count(),
+           "what": "fp32-order C oracle (OpenMP over output rows), median of 3 after one warm-up", "workloads": {}}
+    for name, wl in inputs.WORKLOADS.items():
+        N = oracle.total_comp(wl.cu_seqlens, wl.ratio)
+        kv, sc, ape, dout = inputs.make_tensors(wl, N)
+        args = (inputs.bits(kv), inputs.bits(sc), ape.numpy(), list(wl.cu_seqlens), wl.total_tokens,
+                wl.ratio, wl.coff, wl.head_dim)
+        doutb = inputs.bits(dout)
+        out = np.zeros((N, wl.head_dim), np.uint16)
+        outs = oracle.bwd_outputs(wl.total_tokens, wl.ratio, wl.coff, wl.head_dim, N)
+        ent = {}
+        for threads in (full, 1):
+            oracle.set_num_threads(threads)
+            for leg, fn in (("fwd", lambda: oracle.fwd_f32(*args, out=out)),
+                            ("bwd", lambda: oracle.bwd_f32(*args, doutb, outs=outs))):
+                fn()
+                ts = []
+                for _ in range(3):
+                    t0 = time.perf_counter()
+                    fn()
+                    ts.append(time.perf_counter() - t0)
+                ent[f"{leg}_us_{'all' if threads == full else '1t'}"] = round(statistics.median(ts) * 1e6, 1)
+        oracle.set_num_threads(full)
+        rec["workloads"][name] = ent
+        print(name, ent, flush=True)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,7 +320,13 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph replay timing")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/hbm_counters.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--cpu-table", metavar="OUT.json",
+                    help="time the CPU oracle on every workload (all threads and one thread) and exit")
     args = ap.parse_args()
+
+    if args.cpu_table:
+        cpu_table(args.cpu_table)
+        return
 
     if args.summarize_counters:
         from gated_pooling_amd import inputs

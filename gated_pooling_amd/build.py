@@ -36,19 +36,35 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *(extra_flags or []), "-o", tmp, *SOURCES]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+DEBUG_LIB = os.path.join(HERE, "libcsa_debug.so")
+
+
+def build(verbose: bool = False, extra_flags=None, debug: bool = True) -> str:
+    """Build libcsa.so and, with debug=True, next to it (in a second hipcc
+    process running at the same time) libcsa_debug.so: the same library with
+    -DCSA_DEBUG_OWNERSHIP, whose backward also counts the stores to every
+    dkv/dscore element (used by tests/test_ownership_gpu.py only)."""
+    jobs = [(LIB, [])] + ([(DEBUG_LIB, ["-DCSA_DEBUG_OWNERSHIP"])] if debug else [])
+    procs = []
+    for out, defs in jobs:
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, *FLAGS, *defs, *(extra_flags or []), "-o", tmp, *SOURCES]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((out, tmp, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    failed = []
+    for out, tmp, pr in procs:
+        _, stderr = pr.communicate()
+        err = "\n".join(l for l in stderr.splitlines() if noise not in l)
+        if pr.returncode != 0:
+            failed.append(f"{os.path.basename(out)}: hipcc failed ({pr.returncode}):\n{err}")
+            continue
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+        os.replace(tmp, out)
+    if failed:
+        raise RuntimeError("\n".join(failed))
     return LIB
 
 

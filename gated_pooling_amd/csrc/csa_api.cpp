@@ -51,6 +51,12 @@ namespace {
 
 thread_local std::string g_err;
 
+#ifdef CSA_DEBUG_OWNERSHIP
+// Ownership counters of the debug build (csa_debug_ownership_counters).
+uint32_t* g_own_dkv = nullptr;
+uint32_t* g_own_dsc = nullptr;
+#endif
+
 csa_status_t fail(csa_status_t st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -481,6 +487,10 @@ csa_status_t launch_bwd_grads(const Problem& pr, const Plan& pl, const void* kv,
     bp.main_wgs = pl.bwd_main_wgs;
     bp.partial_rows = pl.partial_rows;
     bp.lds_table_words = pl.lds_table_words;
+#ifdef CSA_DEBUG_OWNERSHIP
+    bp.own_dkv = g_own_dkv;
+    bp.own_dsc = g_own_dsc;
+#endif
     if (!csa::launch_bwd128(pr.coff, bp, pl.bwd.grid, pl.bwd.lds_bytes, stream))
       return fail(CSA_STATUS_NOT_SUPPORTED, "no ratio-128 backward kernel for this configuration");
     return after_launch("backward");
@@ -503,6 +513,10 @@ csa_status_t launch_bwd_grads(const Problem& pr, const Plan& pl, const void* kv,
   bp.main_wgs = pl.bwd_main_wgs;
   bp.partial_rows = pl.partial_rows;
   bp.lds_table_words = pl.lds_table_words;
+#ifdef CSA_DEBUG_OWNERSHIP
+  bp.own_dkv = g_own_dkv;
+  bp.own_dsc = g_own_dsc;
+#endif
   if (!csa::launch_bwd(pr.ratio, pr.coff, bp, pl.bwd, stream))
     return fail(CSA_STATUS_NOT_SUPPORTED, "no backward kernel for this configuration");
   return after_launch("backward");
@@ -699,5 +713,17 @@ csa_status_t csa_compressor_bwd_noalloc(const void* kv, const void* score, const
   if ((st = launch_bwd_grads(pr, pl, kv, score, ape, cu, cu_host, dout, dkv, dscore, ws, stream))) return st;
   return launch_reduce(pr, pl, dape, ws, stream);
 }
+
+#ifdef CSA_DEBUG_OWNERSHIP
+// Debug build only (libcsa_debug.so): device arrays of one uint32 per dkv /
+// dscore element (total_tokens * coff * head_dim each, zeroed by the caller)
+// that every later backward store adds 1 to; NULL, NULL switches counting
+// off.  Not part of the ABI of libcsa.so.
+csa_status_t csa_debug_ownership_counters(uint32_t* dkv_counts, uint32_t* dscore_counts) {
+  g_own_dkv = dkv_counts;
+  g_own_dsc = dscore_counts;
+  return ok();
+}
+#endif
 
 }  // extern "C"

@@ -716,23 +716,45 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
 // Backward: gradients, zero ownership, dAPE partials
 // ---------------------------------------------------------------------------
 
+// Ownership counting (builds with CSA_DEBUG_OWNERSHIP only): every store to
+// dkv or dscore adds 1 to a uint32 counter per element it writes, so a test
+// can check that each slot is written exactly once.  Stores at or past
+// `limit` (masked lanes' past-the-end offsets) write nothing and count
+// nothing.
+__device__ __forceinline__ void own_count(uint32_t* cnt, uint32_t byte_off, uint32_t bytes, uint32_t limit) {
+#ifdef CSA_DEBUG_OWNERSHIP
+  if (cnt != nullptr && byte_off < limit)
+    for (uint32_t e = 0; e < bytes / 2; ++e) atomicAdd(cnt + byte_off / 2 + e, 1u);
+#else
+  (void)cnt;
+  (void)byte_off;
+  (void)bytes;
+  (void)limit;
+#endif
+}
+
 // Zero a byte range [begin, end) of a buffer with 16-byte stores when both
 // ends are 16-byte aligned, 4-byte stores when both are 4-byte aligned,
 // 2-byte stores otherwise (rows of an odd coff * head_dim).  The walk steps
 // an element index (walk_elements), so a range that ends near 2^32 bytes
 // cannot wrap back onto the start of the buffer.
 __device__ __forceinline__ void zero_range(rsrc_t r, uint32_t begin, uint32_t end, uint32_t first,
-                                           uint32_t step) {
+                                           uint32_t step, uint32_t* cnt, uint32_t limit) {
   if (((begin | end) & 15u) == 0) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    walk_elements<16>(begin, end, first, step,
-                      [&](uint32_t o) { __builtin_amdgcn_raw_buffer_store_b128(z, r, o, 0, 0); });
+    walk_elements<16>(begin, end, first, step, [&](uint32_t o) {
+      __builtin_amdgcn_raw_buffer_store_b128(z, r, o, 0, 0);
+      own_count(cnt, o, 16, limit);
+    });
   } else if (((begin | end) & 3u) == 0) {
-    walk_elements<4>(begin, end, first, step,
-                     [&](uint32_t o) { __builtin_amdgcn_raw_buffer_store_b32(0u, r, o, 0, 0); });
+    walk_elements<4>(begin, end, first, step, [&](uint32_t o) {
+      __builtin_amdgcn_raw_buffer_store_b32(0u, r, o, 0, 0);
+      own_count(cnt, o, 4, limit);
+    });
   } else {
     walk_elements<2>(begin, end, first, step, [&](uint32_t o) {
       __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(0), r, o, 0, 0);
+      own_count(cnt, o, 2, limit);
     });
   }
 }
@@ -748,14 +770,14 @@ __device__ void zero_sweep(const Params& p, const SegTable& tab) {
   for (int s = zid; s < S; s += nz) {
     if (tab.off[s + 1] == tab.off[s] && tab.cu[s + 1] > tab.cu[s]) {
       const uint32_t b0 = tab.cu[s] * row_bytes, b1 = tab.cu[s + 1] * row_bytes;
-      zero_range(rdkv, b0, b1, threadIdx.x, NT);
-      zero_range(rdsc, b0, b1, threadIdx.x, NT);
+      zero_range(rdkv, b0, b1, threadIdx.x, NT, p.own_dkv, p.io_bytes);
+      zero_range(rdsc, b0, b1, threadIdx.x, NT, p.own_dsc, p.io_bytes);
     }
   }
   // static-capacity padding rows past cu[S]
   const uint32_t b0 = tab.cu[S] * row_bytes, b1 = static_cast<uint32_t>(p.seg.T_cap) * row_bytes;
-  zero_range(rdkv, b0, b1, zid * NT + threadIdx.x, nz * NT);
-  zero_range(rdsc, b0, b1, zid * NT + threadIdx.x, nz * NT);
+  zero_range(rdkv, b0, b1, zid * NT + threadIdx.x, nz * NT, p.own_dkv, p.io_bytes);
+  zero_range(rdsc, b0, b1, zid * NT + threadIdx.x, nz * NT, p.own_dsc, p.io_bytes);
 }
 
 template <int R, int CO, int C, int NT, int TBL, bool UNI, int PF, bool PAD>
@@ -806,6 +828,11 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   // 0) and store nothing
   const bool active = !PAD || g < p.chunks;
   auto msk = [&](uint32_t o) { return active ? o : p.io_bytes; };
+  // a gradient store (tensor 0: dkv, 1: dscore) of the lane's chunk
+  auto put = [&](int tensor, uint32_t off, const Pack<C>& v) {
+    store_pack<C>(tensor ? rdsc : rdkv, off, v);
+    own_count(tensor ? p.own_dsc : p.own_dkv, off, C * 2, p.io_bytes);
+  };
 
   float ape_r[CO][R][C];
   float acc_r[CO][R][C];
@@ -872,10 +899,10 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        store_pack<C>(rdkv, msk((own - R + i) * rowb + lane_prev), gkv[i]);
-        store_pack<C>(rdsc, msk((own - R + i) * rowb + lane_prev), gsc[i]);
-        store_pack<C>(rdkv, msk((own + i) * rowb + lane_own), gkv[R + i]);
-        store_pack<C>(rdsc, msk((own + i) * rowb + lane_own), gsc[R + i]);
+        put(0, msk((own - R + i) * rowb + lane_prev), gkv[i]);
+        put(1, msk((own - R + i) * rowb + lane_prev), gsc[i]);
+        put(0, msk((own + i) * rowb + lane_own), gkv[R + i]);
+        put(1, msk((own + i) * rowb + lane_own), gsc[R + i]);
       }
     } else {
       Pack<C> gkv[R], gsc[R];
@@ -914,8 +941,8 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        store_pack<C>(rdkv, msk((own + i) * rowb + lane_own), gkv[i]);
-        store_pack<C>(rdsc, msk((own + i) * rowb + lane_own), gsc[i]);
+        put(0, msk((own + i) * rowb + lane_own), gkv[i]);
+        put(1, msk((own + i) * rowb + lane_own), gsc[i]);
       }
     }
     if (cur.last) {
@@ -926,15 +953,15 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       if (CO == 2) {
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-          store_pack<C>(rdkv, msk((own + i) * rowb + lane_prev), z);
-          store_pack<C>(rdsc, msk((own + i) * rowb + lane_prev), z);
+          put(0, msk((own + i) * rowb + lane_prev), z);
+          put(1, msk((own + i) * rowb + lane_prev), z);
         }
       }
       for (uint32_t t = own + R; t < cur.seg_end; ++t) {
 #pragma unroll
         for (int h = 0; h < CO; ++h) {
-          store_pack<C>(rdkv, msk(t * rowb + h * d * 2u + lane_prev), z);
-          store_pack<C>(rdsc, msk(t * rowb + h * d * 2u + lane_prev), z);
+          put(0, msk(t * rowb + h * d * 2u + lane_prev), z);
+          put(1, msk(t * rowb + h * d * 2u + lane_prev), z);
         }
       }
     }
@@ -1469,9 +1496,11 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void bwd128_kernel(Bwd128Para
                                             p.io_bytes);
       const int rq = (it / (S::kIters / 2)) * Wn::kRows + k;
       const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rq * kSlice128 + spart * 8);
-      if (o2 != p.io_bytes)
+      if (o2 != p.io_bytes) {
         __builtin_amdgcn_raw_buffer_store_b128(v, it < S::kIters / 2 ? rdsc : rdkv, o2 + spart * 16u, 0,
                                                kAuxStreamStore);
+        own_count(it < S::kIters / 2 ? p.own_dsc : p.own_dkv, o2 + spart * 16u, 16, p.io_bytes);
+      }
     }
     if (row.last) {
       // the segment's last block owns the never-read slots next to it: its
@@ -1490,6 +1519,7 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void bwd128_kernel(Bwd128Para
           o2 = (row.own + kRatio128 + kt / CO) * row_bytes + (kt % CO) * half_bytes + slice_bytes;
         }
         __builtin_amdgcn_raw_buffer_store_b128(z, tensor ? rdkv : rdsc, o2 + part * 16u, 0, kAuxStreamStore);
+        own_count(tensor ? p.own_dkv : p.own_dsc, o2 + part * 16u, 16, p.io_bytes);
       }
     }
     __syncthreads();  // the next row's staging overwrites stage

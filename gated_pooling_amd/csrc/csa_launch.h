@@ -69,6 +69,8 @@ struct BwdParams {
   uint32_t main_wgs;      // workgroups [0, main_wgs) compute windows, the rest zero-fill
   uint32_t partial_rows;  // main_wgs / slices
   uint32_t lds_table_words;
+  uint32_t* own_dkv;      // ownership counters, one per dkv / dscore element: every store
+  uint32_t* own_dsc;      // adds 1 (builds with CSA_DEBUG_OWNERSHIP only; null otherwise)
 };
 
 // ratio = 128 (windows of 128 * coff rows): a workgroup owns a slice of
@@ -107,6 +109,8 @@ struct Bwd128Params {
   uint32_t main_wgs;      // workgroups [0, main_wgs) compute windows, the rest zero-fill
   uint32_t partial_rows;  // main_wgs / nslices
   uint32_t lds_table_words;
+  uint32_t* own_dkv;      // ownership counters as in BwdParams
+  uint32_t* own_dsc;
 };
 
 struct ReduceParams {

@@ -67,6 +67,8 @@ def lib():
         L.oracle_f32_from_bf16.argtypes = [ctypes.c_uint16]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
+        L.oracle_set_num_threads.restype = None
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         L.oracle_total_comp.restype = ctypes.c_int
         L.oracle_total_comp.argtypes = [P, i32, i32, P]
         L.oracle_fwd_f32.restype = ctypes.c_int
@@ -97,6 +99,11 @@ def _check(rc: int, what: str):
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of later oracle calls."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def total_comp(cu, r: int) -> int:

@@ -157,6 +157,10 @@ void oracle_exp_constants(float* out)
 /* OpenMP threads used by the parallel window loops (reported with timings). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 
+/* Set the number of OpenMP threads of later calls (for the one-thread
+ * timings of the CPU baseline). */
+void oracle_set_num_threads(int n) { if (n > 0) omp_set_num_threads(n); }
+
 /* ---------------------------------------------------------------------- */
 /* Pack bookkeeping                                                        */
 /* ---------------------------------------------------------------------- */
