@@ -101,6 +101,75 @@ ROLE_OF_KERNEL = (("fwd_kernel", "fwd"), ("fwd128_kernel", "fwd"), ("bwd_kernel"
 COPY_BYTES = 512 * 2 ** 20  # the context copy below moves 512 MiB each way
 
 
+def role_of(kernel_name):
+    return next((r for k, r in ROLE_OF_KERNEL if re.search(r"\b" + k + r"[<(]", kernel_name)), None)
+
+
+def profile_rows(d, kind):
+    """Rows of a rocprofv3 output directory, CSV or SQLite (rocpd) format:
+    kind "counters" -> (kernel name, counter name, value) per dispatch;
+    kind "trace" -> (kernel name, duration ns, vgpr, accum vgpr, sgpr, lds bytes, workgroup size, grid size)."""
+    import csv
+    import glob
+    import sqlite3
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+        con = sqlite3.connect(f)
+        if kind == "counters":
+            rows += [(n, c, float(v)) for n, c, v in
+                     con.execute("select kernel_name, counter_name, value from counters_collection")]
+        else:
+            rows += [tuple(r) for r in con.execute(
+                "select name, duration, vgpr_count, accum_vgpr_count, sgpr_count, lds_size, "
+                "workgroup_x * workgroup_y * workgroup_z, grid_x * grid_y * grid_z from kernels")]
+        con.close()
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv" if kind == "counters"
+                                    else "*kernel_trace.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if kind == "counters":
+                rows.append((row["Kernel_Name"], row["Counter_Name"], float(row["Counter_Value"])))
+            else:
+                rows.append((row["Kernel_Name"], int(row["End_Timestamp"]) - int(row["Start_Timestamp"]),
+                             int(row.get("Arch_VGPR_Count", 0)), int(row.get("Accum_VGPR_Count", 0)),
+                             int(row.get("SGPR_Count", 0)), int(row.get("LDS_Block_Size", 0)),
+                             int(row.get("Workgroup_Size", 0)), int(row.get("Grid_Size", 0))))
+    return rows
+
+
+def summarize_trace(d):
+    """Markdown table of a rocprofv3 --kernel-trace run: per kernel instance,
+    dispatches and duration statistics (us), with the dispatch's resources."""
+    import statistics
+    by = {}
+    for name, dur, vg, ag, sg, lds, wg, grid in profile_rows(d, "trace"):
+        e = by.setdefault(name, {"d": [], "res": (vg, ag, sg, lds, wg, grid)})
+        e["d"].append(dur / 1000.0)
+    out = ["| kernel | dispatches | mean us | median us | min us | LDS B | workgroup | grid (threads) |",
+           "|---|---|---|---|---|---|---|---|"]
+    for name, e in sorted(by.items(), key=lambda kv: -sum(kv[1]["d"])):
+        ds = e["d"]
+        short = re.sub(r"\(.*$", "", name.replace("csa::(anonymous namespace)::", "").replace("void ", ""))
+        out.append(f"| `{short}` | {len(ds)} | {statistics.mean(ds):.2f} | {statistics.median(ds):.2f} | "
+                   f"{min(ds):.2f} | " + " | ".join(str(x) for x in e["res"][3:]) + " |")
+    return "\n".join(out)
+
+
+def summarize_occupancy(d):
+    """Markdown table of a rocprofv3 --pmc MeanOccupancyPerCU OccupancyPercent
+    run: per kernel instance, the mean of each counter over its dispatches."""
+    by = {}
+    for name, cname, v in profile_rows(d, "counters"):
+        by.setdefault(name, {}).setdefault(cname, []).append(v)
+    cols = sorted({c for e in by.values() for c in e})
+    out = ["| kernel | dispatches | " + " | ".join(cols) + " |", "|---|---|" + "---|" * len(cols)]
+    for name, e in sorted(by.items()):
+        short = re.sub(r"\(.*$", "", name.replace("csa::(anonymous namespace)::", "").replace("void ", ""))
+        n = max(len(v) for v in e.values())
+        out.append(f"| `{short}` | {n} | " + " | ".join(f"{sum(e[c]) / len(e[c]):.2f}" if c in e else ""
+                                                      for c in cols) + " |")
+    return "\n".join(out)
+
+
 def summarize_counters(fetch_dir, write_dir, workload):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
     WRITE_SIZE; counters in KiB per dispatch) into HBM bytes per launch for
@@ -108,21 +177,16 @@ def summarize_counters(fetch_dir, write_dir, workload):
     keyed by the sha256 of the kernel sources.  Each counter is scaled by what
     it reads for the 512 MiB device-to-device copy that the same run makes
     (known to fetch and to write exactly 512 MiB per dispatch)."""
-    import csv
-    import glob
-
     def per_kernel(d, counter):
         vals = {}
-        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            for row in csv.DictReader(open(f)):
-                if row["Counter_Name"] != counter:
-                    continue
-                name = row["Kernel_Name"]
-                role = next((r for k, r in ROLE_OF_KERNEL if re.search(r"\b" + k + r"[<(]", name)), None)
-                if role is None and "copy" in name.lower():
-                    role = "copy"
-                if role is not None:
-                    vals.setdefault(role, []).append(float(row["Counter_Value"]) * 1024.0)
+        for name, cname, value in profile_rows(d, "counters"):
+            if cname != counter:
+                continue
+            role = role_of(name)
+            if role is None and "copy" in name.lower():
+                role = "copy"
+            if role is not None:
+                vals.setdefault(role, []).append(value * 1024.0)
         if "copy" in vals:  # keep the 512 MiB copies, not the small staging copies of the inputs
             top = max(vals["copy"])
             vals["copy"] = [v for v in vals["copy"] if v >= 0.25 * top]
@@ -320,12 +384,20 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph replay timing")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/hbm_counters.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-trace", metavar="DIR", help="print a kernel-trace summary (markdown) and exit")
+    ap.add_argument("--summarize-occupancy", metavar="DIR", help="print an occupancy summary (markdown) and exit")
     ap.add_argument("--cpu-table", metavar="OUT.json",
                     help="time the CPU oracle on every workload (all threads and one thread) and exit")
     args = ap.parse_args()
 
     if args.cpu_table:
         cpu_table(args.cpu_table)
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_occupancy:
+        print(summarize_occupancy(args.summarize_occupancy))
         return
 
     if args.summarize_counters:
