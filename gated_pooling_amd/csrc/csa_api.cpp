@@ -35,7 +35,7 @@
 //   CSA_FWD_PREFETCH, CSA_BWD_PREFETCH  windows in flight per lane on the
 //                     uniform path (2, 3, 4)
 //   CSA_R128_FWD_WGS, CSA_R128_BWD_WGS  ratio-128 grid caps (default: the
-//                     workgroups the chip holds at once, by coff)
+//                     workgroups the chip holds at once)
 
 #include <stdarg.h>
 #include <stdio.h>
@@ -82,7 +82,7 @@ struct Tuning {
   int uniform = 1;        // wave-uniform row path where a row has >= 64 chunks
   int fwd_prefetch = 2;   // windows in flight per lane (uniform path)
   int bwd_prefetch = 3;
-  int r128_fwd_wgs = 0;   // ratio 128 grid caps (workgroups); 0: by coff
+  int r128_fwd_wgs = 0;   // ratio 128 grid caps (workgroups); 0: the chip's residency
   int r128_bwd_wgs = 0;
 };
 
@@ -213,63 +213,60 @@ int64_t pow2_floor(int64_t x) {
   return p;
 }
 
-// ratio 128: a workgroup per (column slice, group of output rows), the
-// window slice staged in LDS (see the kernels).  Grids are capped at the
-// number of workgroups the chip holds at once.
+// ratio 128: a workgroup per (column slice, group of output rows), rows of a
+// slice dealt round-robin to its workgroups (see the kernels).
+//   forward: two waves per 64-entry chunk, the staged window and two exchange
+//     sets in dynamic LDS after the segment table; two workgroups per CU at
+//     coff 2, four at coff 1 (measured best on 65536-token packs);
+//   backward: 1024 threads, one workgroup per CU (its two static LDS window
+//     buffers take most of the CU's LDS); every workgroup also zero-fills a
+//     share of the never-read rows after its windows, so there are no
+//     separate zero-fill workgroups.  Dynamic LDS: the segment table and the
+//     exchange area.
 Plan make_plan_r128(const Problem& p) {
   const Tuning& tu = tuning();
   Plan pl{};
   const int64_t W = int64_t{p.coff} * p.head_dim;
   pl.global_table = p.S > csa::kMaxLdsSegments;
   pl.off_bytes = pl.global_table ? align_up(uint64_t(p.S + 1) * 4, 256) : 0;
-  const int rows = p.coff * csa::kRatio128;           // window rows
-  const int chunks = rows / csa::kChunk128;
-  const int NT = 2 * chunks * 64;                      // two waves per 64-entry chunk
-  // two exchange sets: wave maxima, part-0 chains, chunk sums
-  const uint64_t red_bytes = 2ull * (2 * chunks * 64 + 4 * chunks * 64) * 4;
-  const uint64_t stage_bytes = 2ull * rows * csa::kSlice128 * 2;   // staged window (score, kv)
-  // the staged window follows the table in LDS and is accessed 16 bytes at a
-  // time: keep it 16-byte aligned
-  const uint32_t table_words =
-      pl.global_table ? 0 : static_cast<uint32_t>(align_up(2 * (NT / 64) + 2 * uint64_t(p.S + 1), 4));
+  // int64 scan scratch [NT/64], cu [S+1], off [S+1]; keeps what follows it
+  // 16-byte aligned
+  auto table_words = [&](int NT) {
+    return pl.global_table ? 0u : static_cast<uint32_t>(align_up(2 * (NT / 64) + 2 * uint64_t(p.S + 1), 4));
+  };
   pl.nslices = static_cast<uint32_t>(p.head_dim / csa::kSlice128);
   const int64_t out_rows = p.N > 0 ? p.N : 1;
-  {
-    // the number of workgroups the chip holds at once (measured best on
-    // 65536-token packs): forward 2 per CU at coff 2, 4 at coff 1
-    const int cap = tu.r128_fwd_wgs ? tu.r128_fwd_wgs : (p.coff == 2 ? 512 : 1024);
+  auto per_slice = [&](int cap) {
     int64_t per = cap / pl.nslices;
     if (per < 1) per = 1;
     if (per > out_rows) per = out_rows;
+    return per;
+  };
+  {
+    const int rows = p.coff * csa::kRatio128;           // window rows
+    const int chunks = rows / csa::kChunk128;
+    const int NT = 2 * chunks * 64;                      // two waves per 64-entry chunk
+    // two exchange sets: wave maxima, part-0 chains, chunk sums
+    const uint64_t red_bytes = 2ull * (2 * chunks * 64 + 4 * chunks * 64) * 4;
+    const uint64_t stage_bytes = 2ull * rows * csa::kSlice128 * 2;   // staged window (score, kv)
+    const int64_t per = per_slice(tu.r128_fwd_wgs ? tu.r128_fwd_wgs : (p.coff == 2 ? 2 : 4) * csa::kCUs);
     pl.fwd.grid = static_cast<uint32_t>(per * pl.nslices);
     pl.fwd.threads = NT;
     pl.fwd.cols = 1;
-    pl.fwd_lds_table_words = table_words;
-    pl.fwd.lds_bytes = table_words * 4ull + stage_bytes + red_bytes;
+    pl.fwd_lds_table_words = table_words(NT);
+    pl.fwd.lds_bytes = pl.fwd_lds_table_words * 4ull + stage_bytes + red_bytes;
     pl.ws_fwd = pl.global_table ? kHeaderBytes + pl.off_bytes : 0;
   }
   {
-    // backward: 2 per CU at coff 2, 3 at coff 1
-    const int cap = tu.r128_bwd_wgs ? tu.r128_bwd_wgs : (p.coff == 2 ? 512 : 768);
-    int64_t per = cap / pl.nslices;
-    if (per < 1) per = 1;
-    if (per > out_rows) per = out_rows;
+    const int64_t per = per_slice(tu.r128_bwd_wgs ? tu.r128_bwd_wgs : csa::kCUs);
     const int64_t main = per * pl.nslices;
-    const int64_t spare_rows = p.T - p.N * p.ratio;
-    int64_t zero = 0;
-    if (spare_rows > 0) {
-      const int64_t bytes = spare_rows * W * 2 * 2;
-      zero = (bytes + int64_t{NT} * 16 * 8 - 1) / (int64_t{NT} * 16 * 8);
-      if (zero < 1) zero = 1;
-      if (zero > 256) zero = 256;
-    }
-    pl.bwd.grid = static_cast<uint32_t>(main + zero);
-    pl.bwd.threads = NT;
+    pl.bwd.grid = static_cast<uint32_t>(main);
+    pl.bwd.threads = csa::kThreads128;
     pl.bwd.cols = 1;
     pl.bwd_main_wgs = static_cast<uint32_t>(main);
     pl.partial_rows = static_cast<uint32_t>(per);
-    pl.lds_table_words = table_words;
-    pl.bwd.lds_bytes = table_words * 4ull + stage_bytes + red_bytes;
+    pl.lds_table_words = table_words(csa::kThreads128);
+    pl.bwd.lds_bytes = pl.lds_table_words * 4ull + csa::kRed128Bytes;
     pl.partial_offset = kHeaderBytes + pl.off_bytes;
     const uint64_t nblk = (uint64_t(p.ratio) * W + csa::kPartBlock - 1) / csa::kPartBlock;
     pl.ws_bwd = pl.partial_offset + align_up(nblk * pl.partial_rows * csa::kPartBlock * 4, 256);

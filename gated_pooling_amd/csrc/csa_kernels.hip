@@ -759,12 +759,12 @@ __device__ __forceinline__ void zero_range(rsrc_t r, uint32_t begin, uint32_t en
   }
 }
 
+// Workgroup zid of nz zero-fills its share of the rows no window reads.
 template <int R, int CO, int NT, typename Params>
-__device__ void zero_sweep(const Params& p, const SegTable& tab) {
+__device__ void zero_sweep(const Params& p, const SegTable& tab, uint32_t zid, uint32_t nz) {
   const uint32_t W = CO * p.head_dim, row_bytes = W * 2u;
   const rsrc_t rdkv = make_rsrc(p.dkv, p.io_bytes);
   const rsrc_t rdsc = make_rsrc(p.dscore, p.io_bytes);
-  const uint32_t zid = blockIdx.x - p.main_wgs, nz = gridDim.x - p.main_wgs;
   const int S = p.seg.S;
   // rows of segments with no output block (L_s < ratio): whole rows
   for (int s = zid; s < S; s += nz) {
@@ -778,6 +778,12 @@ __device__ void zero_sweep(const Params& p, const SegTable& tab) {
   const uint32_t b0 = tab.cu[S] * row_bytes, b1 = static_cast<uint32_t>(p.seg.T_cap) * row_bytes;
   zero_range(rdkv, b0, b1, zid * NT + threadIdx.x, nz * NT, p.own_dkv, p.io_bytes);
   zero_range(rdsc, b0, b1, zid * NT + threadIdx.x, nz * NT, p.own_dsc, p.io_bytes);
+}
+
+// The zero-fill workgroups [main_wgs, grid) of a launch share the sweep.
+template <int R, int CO, int NT, typename Params>
+__device__ void zero_sweep(const Params& p, const SegTable& tab) {
+  zero_sweep<R, CO, NT>(p, tab, blockIdx.x - p.main_wgs, gridDim.x - p.main_wgs);
 }
 
 template <int R, int CO, int C, int NT, int TBL, bool UNI, int PF, bool PAD>
@@ -1145,27 +1151,73 @@ __global__ __launch_bounds__(kReduceNT) void dape_reduce_kernel(ReduceParams p) 
 
 // ---------------------------------------------------------------------------
 // ratio = 128 [PR5984: ratio=128 commit]: a window holds 128 * coff rows per
-// column, too many for one lane's registers.  A workgroup owns a slice of
-// kSlice128 columns (lane = column) and walks output rows.  The window's row
-// slices (score and kv, 128 bytes each) are staged in LDS with 16-byte loads,
-// and each 64-entry summation chunk is held by two waves, 32 entries each
-// (`part` 0 and 1).  Per row:
-//   1. x = score + ape for the wave's 32 entries, the wave's max, exchanged
+// column, too many for one lane's registers, so both kernels stage windows in
+// LDS: a workgroup owns a slice of kSlice128 = 64 columns (lane = column) and
+// walks output rows.  Each lane's window entries are split over the waves
+// (one per 32 entries in the forward, per 8 coff entries in the backward),
+// and per row:
+//   1. x = score + ape for the wave's entries, the wave's max, exchanged
 //      through LDS -> window max m;
-//   2. e = EXP(x - m); part 0 starts the chunk's Z (from its first e) and acc
-//      (fma chain from 0), part 1 continues both chains from part 0's values
-//      (handed over through LDS), so every chunk is summed in entry order;
-//      the chunk sums are then added in chunk order: exactly the chunked fp32
-//      order of windows above 64 entries (the first block at coff 2 has only
-//      the own half: chunks 2 and 3);
-//   backward 3. a = e * R * g, ds = a (v - o), bf16 results written over the
-//      staged inputs in LDS, then stored with 16-byte stores; dAPE sums stay
-//      in registers (a wave always holds the same 32 positions of its slice)
-//      and leave as one partial row per workgroup.
-// The forward loads the next row's window into registers while the current
-// row computes.  head_dim is a multiple of kSlice128, so every row slice is
-// whole.
+//   2. e = EXP(x - m); the entries' Z (adds) and acc (fma chain from 0) are
+//      summed in an order fixed per kernel (below), chains of consecutive
+//      entries first, then the chain sums in window order;
+//   forward 3. out = acc * (1/Z) as bf16;
+//   backward 3. a = e R g, ds = a (v - o) as bf16, written over the staged
+//      inputs in LDS and stored with 16-byte stores; dAPE sums stay in
+//      registers (a wave always holds the same positions of its slice) and
+//      leave as one partial row per workgroup.
+// These summation orders are not the single chain of the ratio 2 and 4
+// kernels: the pages hold ratio 128 to the final bf16 rounding instead of to
+// bit equality [PR5984: ratio=128 commit, numerics contract per ratio family],
+// and include/csa.h states the bound.  head_dim is a multiple of kSlice128,
+// so every slice is whole.
 // ---------------------------------------------------------------------------
+
+// Byte offset in kv/score of window row k's slice, or `oob` when the row is
+// masked (the previous half of a segment's first block).
+template <int CO>
+__device__ __forceinline__ uint32_t row128_offset(int k, uint32_t own, bool has_prev, uint32_t row_bytes,
+                                                  uint32_t half_bytes, uint32_t slice_bytes, uint32_t oob) {
+  if constexpr (CO == 2) {
+    if (k < kRatio128) return has_prev ? (own - kRatio128 + k) * row_bytes + slice_bytes : oob;
+    return (own + k - kRatio128) * row_bytes + half_bytes + slice_bytes;
+  } else {
+    return (own + k) * row_bytes + slice_bytes;
+  }
+}
+
+// Row of output row n (uniform): segment lookup on the scalar unit.  `valid`
+// is false for rows past the pack (the ring's look-ahead copies).
+struct Row128 {
+  uint32_t own, seg_end;
+  bool has_prev, last, valid;
+};
+template <int TBL>
+__device__ __forceinline__ Row128 row128(uint32_t n, uint32_t N, int& s_hint, const UTable<TBL>& t, int S) {
+  Row128 r{};
+  if (n >= N) return r;
+  int lo = s_hint, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (t.off_at(mid) <= n) lo = mid; else hi = mid - 1;
+  }
+  s_hint = lo;
+  const uint32_t o0 = t.off_at(lo), b = n - o0, nb = t.off_at(lo + 1) - o0;
+  r.own = t.cu_at(lo) + b * kRatio128;
+  r.seg_end = t.cu_at(lo + 1);
+  r.has_prev = b > 0;
+  r.last = b + 1 == nb;
+  r.valid = true;
+  return r;
+}
+
+// Forward: two workgroups per CU (a 64 KB staged window each), each 2 waves
+// per 64-entry chunk (32 entries per wave, `part` 0 and 1): part 0 starts the
+// chunk's Z and acc chains, part 1 continues them (handed over through LDS),
+// then the chunk sums are added in chunk order.  The window slices are loaded
+// with 16-byte loads into registers one row ahead and written to LDS while
+// the previous row has finished, so each workgroup keeps one window of loads
+// in flight while it computes, two per CU.
 template <int CO>
 struct Win128 {
   static constexpr int kRows = CO * kRatio128;        // window rows
@@ -1181,39 +1233,6 @@ struct Win128 {
 
 // Byte offset in kv/score of window row k's slice, or `oob` when the row is
 // masked (the previous half of a segment's first block).
-template <int CO>
-__device__ __forceinline__ uint32_t row128_offset(int k, uint32_t own, bool has_prev, uint32_t row_bytes,
-                                                  uint32_t half_bytes, uint32_t slice_bytes, uint32_t oob) {
-  if constexpr (CO == 2) {
-    if (k < kRatio128) return has_prev ? (own - kRatio128 + k) * row_bytes + slice_bytes : oob;
-    return (own + k - kRatio128) * row_bytes + half_bytes + slice_bytes;
-  } else {
-    return (own + k) * row_bytes + slice_bytes;
-  }
-}
-
-// Row of output row n (uniform): segment lookup on the scalar unit.
-struct Row128 {
-  uint32_t own, seg_end;
-  bool has_prev, last;
-};
-template <int TBL>
-__device__ __forceinline__ Row128 row128(uint32_t n, int& s_hint, const UTable<TBL>& t, int S) {
-  int lo = s_hint, hi = S - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (t.off_at(mid) <= n) lo = mid; else hi = mid - 1;
-  }
-  s_hint = lo;
-  const uint32_t o0 = t.off_at(lo), b = n - o0, nb = t.off_at(lo + 1) - o0;
-  Row128 r;
-  r.own = t.cu_at(lo) + b * kRatio128;
-  r.seg_end = t.cu_at(lo + 1);
-  r.has_prev = b > 0;
-  r.last = b + 1 == nb;
-  return r;
-}
-
 // A thread's share of one staged window: kIters 16-byte parts; iterations
 // [0, kIters/2) are score rows, the rest kv rows, so the buffer resource of
 // each load is known at compile time.
@@ -1370,7 +1389,7 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void fwd128_kernel(Fwd128Para
   uint32_t n = __builtin_amdgcn_readfirstlane(blockIdx.x / nslices);
   Row128 row{};
   if (n < N) {
-    row = row128<TBL>(n, s_hint, t, p.seg.S);
+    row = row128<TBL>(n, N, s_hint, t, p.seg.S);
     issue_window128<CO>(st, rsc, rkv, row, row_bytes, half_bytes, slice_bytes, p.io_bytes);
   }
   uint32_t set = 0;
@@ -1380,7 +1399,7 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void fwd128_kernel(Fwd128Para
     const uint32_t nn = n + per_slice;
     Row128 nrow{};
     if (nn < N) {
-      nrow = row128<TBL>(nn, s_hint, t, p.seg.S);
+      nrow = row128<TBL>(nn, N, s_hint, t, p.seg.S);
       issue_window128<CO>(st, rsc, rkv, nrow, row_bytes, half_bytes, slice_bytes, p.io_bytes);
     }
     const bool present = wv.present(row);
@@ -1399,140 +1418,374 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void fwd128_kernel(Fwd128Para
   }
 }
 
-template <int CO, int TBL>
-__global__ __launch_bounds__(Win128<CO>::kThreads) void bwd128_kernel(Bwd128Params p) {
-  using Wn = Win128<CO>;
-  using S = Stage128<CO>;
-  constexpr int NT = Wn::kThreads, K = Wn::kPart;
-  extern __shared__ int32_t lds[];
-  SegTable tab{nullptr, nullptr};
-  bool valid = true;
-  if constexpr (TBL == kTableArgs) {
-    if (blockIdx.x >= p.main_wgs) load_segment_table<kRatio128, NT, TBL>(p.seg, lds, tab);
+// ---------------------------------------------------------------------------
+// Backward: one workgroup of 16 waves per CU, wave w holding entries
+// [8 coff w, 8 coff (w+1)) of its lane's column; each wave sums its entries
+// in entry order, then the 16 wave sums are added in wave order.  Each row's
+// window (score and kv, 128 bytes per window row) and dout slice are copied
+// from memory into LDS by the buffer unit itself (buffer_load ... lds: no
+// registers, no LDS write instructions) into one of two buffers while the
+// previous row computes from the other, so the gradient arithmetic and
+// stores of one row overlap the loads of the next.  The staged window is laid
+// out by wave (wave w's score rows, then its kv rows), which is also what
+// wave w copies, so a wave copies, reads, overwrites and stores only its own
+// rows and the store needs no barrier.
+//
+// Waits.  An LDS copy counts in the issuing wave's vector-memory counter like
+// a load and completes in issue order with the wave's other vector memory
+// operations, so "row i's copy has landed" is `s_waitcnt vmcnt(k)` with k the
+// number of vector memory operations this wave issued after that copy,
+// followed by a barrier for the other waves' copies.  k is fixed by the code:
+// every row issues the same copies and stores (copies past the last row and
+// stores of masked rows use offsets past the buffer's range: the copy writes
+// zeros, the store writes nothing); the segment-tail zero stores come after
+// and only make a wait longer; the first row, with fewer operations behind
+// it, waits for all.  There is no __syncthreads() in the row loop: its fence
+// would wait for the copy in flight.
+template <int CO>
+struct R128 {
+  static constexpr int kRows = CO * kRatio128;               // window entries per column
+  static constexpr int kWaves = kThreads128 / 64;            // 16
+  static constexpr int kCols = kSlice128;                    // columns of a row slice (lane = column)
+  static constexpr int kE = kRows / kWaves;                  // entries per lane = window rows per wave
+  static constexpr int kRowBytes = kCols * 2;                // one staged row slice: 128 bytes
+  static constexpr int kWaveBytes = 2 * kE * kRowBytes;      // a wave's score rows then kv rows
+  static constexpr int kCopies = kWaveBytes / 1024;          // 16-byte-per-lane copies per wave
+  static constexpr int kStageBytes = kWaves * kWaveBytes;
+  static constexpr int kBufBytes = kStageBytes + kRowBytes;  // + the dout row slice
+  static constexpr int kBufs = 2;
+  static_assert(kE % (1024 / kRowBytes) == 0, "a copy is one tensor's rows");
+};
+
+using lds_void_t = __attribute__((address_space(3))) void;
+
+// Buffer descriptor words (as make_rsrc builds them) for the copies below,
+// which take the descriptor as four scalar registers.
+__device__ __forceinline__ u32x4 rsrc_words(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return u32x4{static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a))),
+               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32) & 0xFFFFu)),
+               bytes, static_cast<uint32_t>(kRsrcWord3)};
+}
+
+// Wait until at most N vector memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+#endif
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its vector memory operations (copies in flight).
+__device__ __forceinline__ void lds_barrier() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#endif
+}
+
+// One 16-byte-per-lane copy from a buffer into LDS (buffer_load_dwordx4 ...
+// lds, non-temporal): active lane l's 16 bytes land at lds + 16 l (lds is
+// wave-uniform, passed in M0); an out-of-range lane writes zeros.  Written in
+// asm so that the compiler does not track the copy: its own wait insertion
+// would otherwise wait for every copy in flight before each LDS read it
+// cannot tell apart from a copy's target.  The copy has no register result;
+// its completion is awaited explicitly (wait_vmem) before a barrier.  Nothing
+// else in these kernels uses M0.  (The host pass of this file compiles an
+// empty body that never runs.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved: see above
+__device__ __forceinline__ void lds_copy16(const u32x4& rsrc, const void* lds, uint32_t byte_off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t base =
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)lds)));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :
+               : "s"(base), "v"(byte_off), "s"(rsrc)
+               : "memory", "m0");
+#else
+  (void)rsrc;
+  (void)lds;
+  (void)byte_off;
+#endif
+}
+#pragma clang diagnostic pop
+
+// The compiler tracks only its own loads: waiting for all of them (and the
+// first items' copies, already issued) before the item loop keeps its waits
+// for the APE registers out of the loop, where they would also wait for
+// copies.
+__device__ __forceinline__ void prologue_wait() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("" ::: "memory");
+}
+
+// Global byte offset of this lane's part of copy j of its wave (or oob):
+// byte 1024 j + 16 lane of the wave's staged block is row slice
+// r = (1024 j + 16 lane) / kRowBytes (score rows first, then kv rows), bytes
+// 16 (lane % (kRowBytes / 16)) of it.
+template <int CO>
+__device__ __forceinline__ uint32_t copy_offset128(int j, const Row128& row, uint32_t row_bytes, uint32_t half_bytes,
+                                                   uint32_t slice_bytes, uint32_t oob) {
+  using Rw = R128<CO>;
+  constexpr uint32_t kLanesPerRow = Rw::kRowBytes / 16;
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t r = (1024u * j + 16u * lane) / Rw::kRowBytes, lr = r % Rw::kE;
+  const int k = static_cast<int>(wave * Rw::kE + lr);
+  if (!row.valid) return oob;
+  const uint32_t o = row128_offset<CO>(k, row.own, CO == 2 && row.has_prev, row_bytes, half_bytes, slice_bytes, oob);
+  return o == oob ? oob : o + (lane % kLanesPerRow) * 16u;
+}
+// tensor of copy j of a wave: score (0) or kv (1)
+template <int CO>
+__device__ __forceinline__ constexpr uint32_t copy_tensor128(int j) {
+  return (1024u * j / R128<CO>::kRowBytes) / R128<CO>::kE;
+}
+
+// Issue the LDS copies of one item's window into `buf` (no wait); each copy
+// is all score or all kv rows of the wave's block.
+template <int CO>
+__device__ __forceinline__ void copy_window128(uint8_t* buf, const u32x4& wsc, const u32x4& wkv, const Row128& row,
+                                               uint32_t row_bytes, uint32_t half_bytes, uint32_t slice_bytes,
+                                               uint32_t oob) {
+  using Rw = R128<CO>;
+  uint8_t* wb = buf + (threadIdx.x >> 6) * Rw::kWaveBytes;
+#pragma unroll
+  for (int j = 0; j < Rw::kCopies; ++j)
+    lds_copy16(copy_tensor128<CO>(j) == 0 ? wsc : wkv, wb + 1024 * j,
+               copy_offset128<CO>(j, row, row_bytes, half_bytes, slice_bytes, oob));
+}
+
+// 16-byte stores of a wave's staged block back to where copy j read it
+// (masked rows: past the range, written nowhere).
+template <int CO>
+__device__ __forceinline__ void store_block128(const uint8_t* wb, int j, const Row128& row, rsrc_t rdsc, rsrc_t rdkv,
+                                               uint32_t row_bytes, uint32_t half_bytes, uint32_t slice_bytes,
+                                               uint32_t oob, uint32_t* own_dsc, uint32_t* own_dkv) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t o = copy_offset128<CO>(j, row, row_bytes, half_bytes, slice_bytes, oob);
+  const u32x4 v = *reinterpret_cast<const u32x4*>(wb + 1024 * j + 16 * lane);
+  constexpr bool kScore = copy_tensor128<CO>(0) == 0;
+  (void)kScore;
+  if (copy_tensor128<CO>(j) == 0) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, rdsc, o, 0, kAuxStreamStore);
+    own_count(own_dsc, o, 16, oob);
   } else {
-    valid = load_segment_table<kRatio128, NT, TBL>(p.seg, lds, tab);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rdkv, o, 0, kAuxStreamStore);
+    own_count(own_dkv, o, 16, oob);
   }
+}
+
+// Window max of the lane's column: the lane's max, then the wave maxima
+// through red[0, 16*64) (waves without entries pass -inf).
+template <int CO>
+__device__ __forceinline__ float window_max128(const float (&x)[R128<CO>::kE], bool present, int wave, int lane,
+                                               float* red) {
+  constexpr int E = R128<CO>::kE, NC = kSlice128;
+  float mw = -__builtin_inff();
+  if (present) {
+    mw = x[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) mw = fmaxf(mw, x[e]);
+  }
+  red[wave * NC + lane] = mw;
+  lds_barrier();
+  float m = red[lane];
+#pragma unroll
+  for (int w = 1; w < R128<CO>::kWaves; ++w) m = fmaxf(m, red[w * NC + lane]);
+  return m;
+}
+
+// e = EXP(x - m) in place; the lane's Z and acc chains into red (Z at
+// [16*64, 32*64), acc at [32*64, 48*64)); waves without entries write 0.
+template <int CO>
+__device__ __forceinline__ void wave_sums128(float (&x)[R128<CO>::kE], const uint16_t* sv, float m, bool present,
+                                             int wave, int lane, float* red) {
+  constexpr int E = R128<CO>::kE, NC = kSlice128, NW = R128<CO>::kWaves;
+  float zl = 0.0f, al = 0.0f;
+  if (present) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = csa_exp(x[e] - m);
+    zl = x[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) zl = zl + x[e];
+#pragma unroll
+    for (int e = 0; e < E; ++e) al = __builtin_fmaf(x[e], __uint_as_float(uint32_t(sv[64 * e]) << 16), al);
+  }
+  red[(NW + wave) * NC + lane] = zl;
+  red[(2 * NW + wave) * NC + lane] = al;
+}
+
+// Z and acc of the window: wave sums added in wave order from the first wave
+// with entries (after the barrier that follows wave_sums128).
+template <int CO>
+__device__ __forceinline__ void window_sums128(bool has_prev, int lane, const float* red, float& Z, float& acc) {
+  constexpr int NW = R128<CO>::kWaves, NC = kSlice128;
+  const int w0 = (CO == 2 && !has_prev) ? NW / 2 : 0, c = lane;
+  Z = red[(NW + w0) * NC + c];
+  acc = red[(2 * NW + w0) * NC + c];
+  for (int w = w0 + 1; w < NW; ++w) {
+    Z = Z + red[(NW + w) * NC + c];
+    acc = acc + red[(2 * NW + w) * NC + c];
+  }
+}
+
+// Wait for item i's copies: after them this wave issued the copies of the
+// next kBufs - 2 items (CP operations each) and, once i >= kBufs - 1, the
+// stores of the kBufs - 1 previous items (ST each); earlier items wait for
+// the copies alone (longer than needed, never shorter).
+template <int CO, int CP, int ST>
+__device__ __forceinline__ void wait_item(uint32_t i) {
+  constexpr int NB = R128<CO>::kBufs;
+  if (i + 1 >= NB) wait_vmem<(NB - 2) * CP + (NB - 1) * ST>();
+  else wait_vmem<(NB - 2) * CP>();
+}
+
+template <int CO, int TBL>
+__global__ __launch_bounds__(kThreads128) void bwd128_kernel(Bwd128Params p) {
+  using Rw = R128<CO>;
+  constexpr int NT = kThreads128, E = Rw::kE, NB = Rw::kBufs, NC = kSlice128;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NB * Rw::kBufBytes];
+  extern __shared__ int32_t lds[];  // [table][exchange]
+  SegTable tab{nullptr, nullptr};
+  // every workgroup walks the LDS table in the zero sweep after its items
+  const bool valid = load_segment_table<kRatio128, NT, TBL>(p.seg, lds, tab);
   if (TBL != kTableGlobal && blockIdx.x == 0 && threadIdx.x == 0) __builtin_nontemporal_store(valid ? 1 : 0, p.ws_flag);
   if (!valid) return;
-  if (blockIdx.x >= p.main_wgs) {
-    zero_sweep<kRatio128, CO, NT>(p, tab);
-    return;
-  }
-  // LDS: [table][staged window][two exchange sets]
-  uint16_t* stage = reinterpret_cast<uint16_t*>(lds + p.lds_table_words);
-  float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(stage) + Wn::kStageBytes);
+  float* red = reinterpret_cast<float*>(lds + p.lds_table_words);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const Wave128<CO> wv(wave);
   const uint32_t d = p.head_dim, W = CO * d, N = static_cast<uint32_t>(p.seg.N);
-  const uint32_t nslices = p.nslices, slice = blockIdx.x % nslices, per_slice = p.main_wgs / nslices;
+  const uint32_t nslices = p.nslices, slice = blockIdx.x % nslices, stride = gridDim.x / nslices;
   const uint32_t wg_in_slice = blockIdx.x / nslices;
-  const uint32_t col = slice * kSlice128 + lane;
-  const rsrc_t rkv = make_rsrc(p.kv, p.io_bytes);
-  const rsrc_t rsc = make_rsrc(p.score, p.io_bytes);
+  const uint32_t col = slice * NC + lane;
   const rsrc_t rdkv = make_rsrc(p.dkv, p.io_bytes);
   const rsrc_t rdsc = make_rsrc(p.dscore, p.io_bytes);
   const rsrc_t rape = make_rsrc(p.ape, kRatio128 * W * 4u);
-  const rsrc_t rdo = make_rsrc(p.dout, N * d * 2u);
-  // APE: held in registers at coff 1; at coff 2 it is read again for every
-  // row (from the cache), which keeps the kernel at 4 waves per SIMD
-  constexpr bool kApeRegs = CO == 1;
-  const uint32_t ape_off = (wv.pos0 * W + wv.half * d + col) * 4u;
-  float ape_r[K], dape_r[K];
+  const u32x4 wkv = rsrc_words(p.kv, p.io_bytes), wsc = rsrc_words(p.score, p.io_bytes);
+  const uint32_t dout_bytes = N * d * 2u;
+  const u32x4 wdo = rsrc_words(p.dout, dout_bytes);
+  const uint32_t kw = wave * Rw::kE, half = CO == 2 ? kw / kRatio128 : 0;
+  const bool prev_half = CO == 2 && half == 0;
+  float ape_r[E], dape_r[E];
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    if constexpr (kApeRegs) ape_r[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rape, ape_off, k * W * 4u, 0));
-    dape_r[k] = 0.0f;
+  for (int e = 0; e < E; ++e) {
+    const uint32_t pos = (kw + e) % kRatio128;
+    ape_r[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rape, (pos * W + half * d + col) * 4u, 0, 0));
+    dape_r[e] = 0.0f;
   }
-  uint16_t* ss = stage + wv.k0 * kSlice128 + lane;
-  uint16_t* sv = stage + (Wn::kRows + wv.k0) * kSlice128 + lane;
 
   const UTable<TBL> t{p.seg, tab.cu, tab.off};
   int s_hint = 0;
-  const uint32_t row_bytes = W * 2u, half_bytes = d * 2u, slice_bytes = slice * kSlice128 * 2u;
-  const uint32_t spart = threadIdx.x % S::kParts;
-  uint32_t set = 0;
-  for (uint32_t n = __builtin_amdgcn_readfirstlane(wg_in_slice); n < N; n += per_slice, set ^= 1u) {
-    const Row128 row = row128<TBL>(n, s_hint, t, p.seg.S);
-    {
-      Stage128<CO> st;
-      issue_window128<CO>(st, rsc, rkv, row, row_bytes, half_bytes, slice_bytes, p.io_bytes);
-      write_window128<CO>(stage, st);
+  const uint32_t row_bytes = W * 2u, half_bytes = d * 2u, slice_bytes = slice * NC * 2u;
+  // one item's copies: the window, and (wave 0, one 16-byte part per lane) the
+  // dout row slice
+  auto copy_item = [&](uint8_t* buf, const Row128& r, uint32_t nr) {
+    copy_window128<CO>(buf, wsc, wkv, r, row_bytes, half_bytes, slice_bytes, p.io_bytes);
+    if (wave == 0 && lane < Rw::kRowBytes / 16)
+      lds_copy16(wdo, buf + Rw::kStageBytes, r.valid ? (nr * d + slice * NC) * 2u + lane * 16u : dout_bytes);
+  };
+  uint32_t n = __builtin_amdgcn_readfirstlane(wg_in_slice);
+  if (n < N) {
+    Row128 ahead[NB - 1];
+#pragma unroll
+    for (int a = 0; a < NB - 1; ++a) {
+      ahead[a] = row128<TBL>(n + a * stride, N, s_hint, t, p.seg.S);
+      copy_item(ring + a * Rw::kBufBytes, ahead[a], n + a * stride);
     }
-    const float g = __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rdo, (n * d + col) * 2u, 0, 0)) << 16);
-    if constexpr (!kApeRegs) {
+    prologue_wait();
+    for (uint32_t i = 0;; ++i) {
+      uint8_t* cur = ring + (i % NB) * Rw::kBufBytes;
+      // wave 0 issues one more copy per item (dout); every wave stores
+      // kCopyOps gradient blocks per item
+      if (wave == 0) wait_item<CO, Rw::kCopies + 1, Rw::kCopies>(i);
+      else wait_item<CO, Rw::kCopies, Rw::kCopies>(i);
+      lds_barrier();  // the item is in LDS; every wave is done with item i - 1
+      const Row128 row = ahead[0];
+      {
+        const uint32_t nn = n + (NB - 1) * stride;
+        const Row128 nxt = row128<TBL>(nn, N, s_hint, t, p.seg.S);
+        copy_item(ring + ((i + NB - 1) % NB) * Rw::kBufBytes, nxt, nn);
 #pragma unroll
-      for (int k = 0; k < K; ++k)
-        ape_r[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rape, ape_off, k * W * 4u, 0));
-    }
-    __syncthreads();
-    const bool present = wv.present(row);
-    float x[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) x[k] = __uint_as_float(uint32_t(ss[k * kSlice128]) << 16) + ape_r[k];
-    float Z, acc;
-    softmax128<CO>(x, sv, present, row.has_prev, wave, lane, wv, red + set * Wn::kRedFloats, Z, acc);
-    const float R = 1.0f / Z;
-    const float o = acc * R;
-    const float G = R * g;
-    if (present) {
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const float v = __uint_as_float(uint32_t(sv[k * kSlice128]) << 16);
-        const float a = x[k] * G;
-        const float ds = a * (v - o);
-        dape_r[k] += ds;
-        const uint32_t ab = pack_bf16x2(a, ds);
-        sv[k * kSlice128] = static_cast<uint16_t>(ab & 0xFFFFu);  // dKV over kv
-        ss[k * kSlice128] = static_cast<uint16_t>(ab >> 16);      // dScore over score
+        for (int a = 0; a < NB - 2; ++a) ahead[a] = ahead[a + 1];
+        ahead[NB - 2] = nxt;
       }
-    }
-    __syncthreads();
-    // store the gradient slices where the window came from (masked rows: none)
+      const bool present = !(prev_half && !row.has_prev);
+      uint8_t* wb = cur + wave * Rw::kWaveBytes;
+      uint16_t* sx = reinterpret_cast<uint16_t*>(wb) + lane;
+      uint16_t* sv = sx + Rw::kE * NC;
+      float x[E];
 #pragma unroll
-    for (int it = 0; it < S::kIters; ++it) {
-      const int k = S::row_of(it);
-      const uint32_t o2 = row128_offset<CO>(k, row.own, CO == 2 && row.has_prev, row_bytes, half_bytes, slice_bytes,
-                                            p.io_bytes);
-      const int rq = (it / (S::kIters / 2)) * Wn::kRows + k;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rq * kSlice128 + spart * 8);
-      if (o2 != p.io_bytes) {
-        __builtin_amdgcn_raw_buffer_store_b128(v, it < S::kIters / 2 ? rdsc : rdkv, o2 + spart * 16u, 0,
-                                               kAuxStreamStore);
-        own_count(it < S::kIters / 2 ? p.own_dsc : p.own_dkv, o2 + spart * 16u, 16, p.io_bytes);
-      }
-    }
-    if (row.last) {
-      // the segment's last block owns the never-read slots next to it: its
-      // own rows' first half (coff 2) and the seqlen % 128 tail rows
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      const uint32_t tail = row.seg_end - (row.own + kRatio128);
-      const uint32_t nz = (CO == 2 ? kRatio128 : 0) + tail * CO;   // row slices to zero
-      for (uint32_t q = threadIdx.x; q < 2 * nz * S::kParts; q += NT) {
-        const uint32_t part = q % S::kParts, rq = q / S::kParts;
-        const uint32_t tensor = rq / nz, k = rq % nz;
-        uint32_t o2;
-        if (CO == 2 && k < kRatio128) {
-          o2 = (row.own + k) * row_bytes + slice_bytes;
-        } else {
-          const uint32_t kt = k - (CO == 2 ? kRatio128 : 0);
-          o2 = (row.own + kRatio128 + kt / CO) * row_bytes + (kt % CO) * half_bytes + slice_bytes;
+      for (int e = 0; e < E; ++e) x[e] = __uint_as_float(uint32_t(sx[64 * e]) << 16) + ape_r[e];
+      const float m = window_max128<CO>(x, present, wave, lane, red);
+      wave_sums128<CO>(x, sv, m, present, wave, lane, red);
+      lds_barrier();
+      float Z, acc;
+      window_sums128<CO>(row.has_prev, lane, red, Z, acc);
+      const float g = __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(cur + Rw::kStageBytes)[lane])
+                                      << 16);
+      const float R = 1.0f / Z;
+      const float o = acc * R;
+      const float G = R * g;
+      if (present) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float v = __uint_as_float(uint32_t(sv[64 * e]) << 16);
+          const float a = x[e] * G;
+          const float ds = a * (v - o);
+          dape_r[e] += ds;
+          const uint32_t ab = pack_bf16x2(a, ds);
+          sv[64 * e] = static_cast<uint16_t>(ab & 0xFFFFu);  // dKV over kv
+          sx[64 * e] = static_cast<uint16_t>(ab >> 16);      // dScore over score
         }
-        __builtin_amdgcn_raw_buffer_store_b128(z, tensor ? rdkv : rdsc, o2 + part * 16u, 0, kAuxStreamStore);
-        own_count(tensor ? p.own_dkv : p.own_dsc, o2 + part * 16u, 16, p.io_bytes);
       }
+      // the wave's own staged rows go back where they came from (same wave:
+      // its LDS writes above are ordered before these reads)
+#pragma unroll
+      for (int j = 0; j < Rw::kCopies; ++j)
+        store_block128<CO>(wb, j, row, rdsc, rdkv, row_bytes, half_bytes, slice_bytes, p.io_bytes, p.own_dsc,
+                           p.own_dkv);
+      if (row.last) {
+        // the segment's last block owns the never-read slots next to it: its
+        // own rows' first half (coff 2) and the seqlen % 128 tail rows
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        constexpr uint32_t kParts = NC * 2 / 16;
+        const uint32_t tail = row.seg_end - (row.own + kRatio128);
+        const uint32_t nz = (CO == 2 ? kRatio128 : 0) + tail * CO;  // row slices to zero
+        for (uint32_t q = threadIdx.x; q < 2 * nz * kParts; q += NT) {
+          const uint32_t part = q % kParts, rq = q / kParts;
+          const uint32_t tensor = rq / nz, k = rq % nz;
+          uint32_t o2;
+          if (CO == 2 && k < kRatio128) {
+            o2 = (row.own + k) * row_bytes + slice_bytes;
+          } else {
+            const uint32_t kt = k - (CO == 2 ? kRatio128 : 0);
+            o2 = (row.own + kRatio128 + kt / CO) * row_bytes + (kt % CO) * half_bytes + slice_bytes;
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(z, tensor ? rdkv : rdsc, o2 + part * 16u, 0, kAuxStreamStore);
+          own_count(tensor ? p.own_dkv : p.own_dsc, o2 + part * 16u, 16, p.io_bytes);
+        }
+      }
+      n += stride;
+      if (n >= N) break;
     }
-    __syncthreads();  // the next row's staging overwrites stage
+    wait_vmem<0>();  // the look-ahead copies land before the workgroup's LDS is released
   }
+  // never-read rows outside every window (segments shorter than 128, rows
+  // past cu[S]): shared by all workgroups
+  zero_sweep<kRatio128, CO, NT>(p, tab, blockIdx.x, gridDim.x);
   // dAPE: one partial row per workgroup of a slice (column-block layout)
   const uint32_t prow = p.partial_rows;
   const uint32_t nblk = (kRatio128 * W + kPartBlock - 1) / kPartBlock;
   const rsrc_t rpart = make_rsrc(p.partials, nblk * prow * kPartBlock * 4u);
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const uint32_t j = (wv.pos0 + k) * W + wv.half * d + col;
+  for (int e = 0; e < E; ++e) {
+    const uint32_t pos = (kw + e) % kRatio128;
+    const uint32_t j = pos * W + half * d + col;
     const uint32_t o2 = ((j / kPartBlock) * prow + wg_in_slice) * kPartBlock + (j % kPartBlock);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dape_r[k]), rpart, o2 * 4u, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dape_r[e]), rpart, o2 * 4u, 0, 0);
   }
 }
 
@@ -1728,7 +1981,7 @@ static void launch_fwd128_c(const Fwd128Params& p, uint32_t grid, size_t lds_byt
 
 template <int CO>
 static void launch_bwd128_c(const Bwd128Params& p, uint32_t grid, size_t lds_bytes, hipStream_t st) {
-  const dim3 g(grid), b(Win128<CO>::kThreads);
+  const dim3 g(grid), b(kThreads128);
   if (p.seg.table == kTableGlobal)
     hipLaunchKernelGGL((bwd128_kernel<CO, kTableGlobal>), g, b, lds_bytes, st, p);
   else if (p.seg.table == kTableArgs)

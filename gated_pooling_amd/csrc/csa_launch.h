@@ -74,12 +74,19 @@ struct BwdParams {
 };
 
 // ratio = 128 (windows of 128 * coff rows): a workgroup owns a slice of
-// kSlice128 columns (one per lane) and walks output rows; the window slice is
-// staged in LDS and each summation chunk of kChunk128 window entries is held
-// by two waves (half the entries each).
+// kSlice128 columns (one per lane) and walks output rows; head_dim must be a
+// multiple of kSlice128.  Forward: the window slice is staged in LDS and each
+// summation chunk of kChunk128 entries is held by two waves; two workgroups
+// per CU.  Backward: workgroups of kThreads128 threads, one per CU (grids
+// capped at kCUs), each window copied into one of two static LDS buffers;
+// kRed128Bytes is its dynamic LDS exchange area after the segment table
+// (wave maxima, wave Z, wave acc).
 constexpr int kRatio128 = 128;
 constexpr int kSlice128 = 64;
 constexpr int kChunk128 = 64;
+constexpr int kThreads128 = 1024;
+constexpr int kRed128Bytes = 3 * (kThreads128 / 64) * kSlice128 * 4;
+constexpr int kCUs = 256;  // MI355X
 
 struct Fwd128Params {
   SegParams seg;
@@ -106,7 +113,7 @@ struct Bwd128Params {
   uint32_t io_bytes;
   uint32_t head_dim;
   uint32_t nslices;
-  uint32_t main_wgs;      // workgroups [0, main_wgs) compute windows, the rest zero-fill
+  uint32_t main_wgs;      // = the grid: every workgroup computes windows, then zero-fills its share
   uint32_t partial_rows;  // main_wgs / nslices
   uint32_t lds_table_words;
   uint32_t* own_dkv;      // ownership counters as in BwdParams

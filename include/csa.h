@@ -34,8 +34,9 @@
  *   from 0;  o = acc*R;  out = bf16_rne(o);  backward: G = R*f32(dout),
  *   a = e*G, dkv = bf16_rne(a), ds = a*(v - o), dscore = bf16_rne(ds).
  *   At ratio 2 and 4 the kernels evaluate exactly this order.  At ratio 128
- *   (windows of 128 or 256 entries) they sum Z and acc per chunk of 64
- *   consecutive entries in this order and then add the chunk sums in chunk
+ *   (windows of 128 or 256 entries) they sum Z and acc in chains of
+ *   consecutive entries in this order (the forward: chunks of 64 entries;
+ *   the backward: 8 * coff entries) and then add the chain sums in window
  *   order ([PR5984: ratio=128 commit]: per-chunk partials merged in one fixed
  *   order), which is still fixed (bit-identical run to run) but differs from
  *   the single chain above by the rounding of the reordered sums: out, dkv

@@ -2,12 +2,14 @@
 window in different orders (ratio 128).
 
 The oracle sums every window in one chain in window order; the ratio-128
-kernels sum 64-entry chunks and then add the chunk sums [PR5984: ratio=128
-commit: per-chunk partials merged in one fixed order].  Both evaluate the same
-x, max and EXP (those are order-free), so the results differ only by the
-rounding of the reordered sums.  For a window of K entries with u = 2^-24,
-standard error analysis of the two K-term sums (Z = sum e, acc = sum e v)
-gives, between the two fp32 evaluations:
+kernels sum chains of consecutive entries (64-entry chunks in the forward,
+8 * coff entries in the backward) and then add the chain sums
+[PR5984: ratio=128 commit: per-chunk partials merged in one fixed order].
+Both evaluate the same x, max and EXP (those are order-free), so the results
+differ only by the rounding of the reordered sums.  For a window of K entries
+with u = 2^-24, the standard error bound of a K-term fp32 sum, which holds for
+any summation order (each term passes through at most K - 1 roundings),
+gives, between the two fp32 evaluations of Z = sum e and acc = sum e v:
 
   |dZ| / Z          <= 2 (K - 1) u
   |d acc|           <= 2 K u sum|e v|
