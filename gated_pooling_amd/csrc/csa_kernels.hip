@@ -1419,7 +1419,8 @@ __global__ __launch_bounds__(Win128<CO>::kThreads) void fwd128_kernel(Fwd128Para
 }
 
 // ---------------------------------------------------------------------------
-// Backward: one workgroup of 16 waves per CU, wave w holding entries
+// Backward (an "item" below is one output row of the workgroup's column
+// slice): one workgroup of 16 waves per CU, wave w holding entries
 // [8 coff w, 8 coff (w+1)) of its lane's column; each wave sums its entries
 // in entry order, then the 16 wave sums are added in wave order.  Each row's
 // window (score and kv, 128 bytes per window row) and dout slice are copied
@@ -1699,7 +1700,7 @@ __global__ __launch_bounds__(kThreads128) void bwd128_kernel(Bwd128Params p) {
     for (uint32_t i = 0;; ++i) {
       uint8_t* cur = ring + (i % NB) * Rw::kBufBytes;
       // wave 0 issues one more copy per item (dout); every wave stores
-      // kCopyOps gradient blocks per item
+      // kCopies gradient blocks per item
       if (wave == 0) wait_item<CO, Rw::kCopies + 1, Rw::kCopies>(i);
       else wait_item<CO, Rw::kCopies, Rw::kCopies>(i);
       lds_barrier();  // the item is in LDS; every wave is done with item i - 1
