@@ -300,6 +300,14 @@ def _r128_cases():
     cases.append((lengths, int(sum(lengths)) + 7, 1, 64, 951, False))
     cases.append(([300, 260, 7], 600, 2, 1024, 952, True))              # largest head_dim: 16 slices
     cases.append(([129, 400], 560, 1, 960, 953, False))                 # 15 slices
+    # long segments with tails: several windows per workgroup of the
+    # one-workgroup-per-CU backward (the copy ring's steady state), segment
+    # ends and their zero tails at every position of the ring
+    for i, (c, d) in enumerate([(2, 64), (1, 64), (2, 128), (1, 320), (2, 512), (2, 192)]):
+        nseg = int(rng.integers(3, 40))
+        lengths = rng.integers(1000, 9000, size=nseg).tolist()
+        T = int(sum(lengths)) + int(rng.integers(1, 500))
+        cases.append((lengths, T, c, d, 960 + i, bool(i % 2)))
     return cases
 
 
