@@ -14,7 +14,8 @@ also compared bit for bit with libcsa.so's on the same inputs.  Packs: the
 ragged packs at ratio 2, 4 and 128 with coff 1 and 2 (tails, a 1-token and a
 (ratio-1)-token segment, an empty segment, padding rows), packs with no output
 row at all (only zero workgroups store), odd and padded head_dims (16- and
-32-bit stores), and a 3000-segment pack (segment table in the workspace).
+32-bit stores), a 3000-segment pack (segment table in the workspace), and
+long ratio-128 packs with several windows per backward workgroup.
 """
 from __future__ import annotations
 
@@ -78,6 +79,10 @@ CASES = {
     "padded_d192_r4_c2": lambda: inputs.custom("np2", [300, 3, 501], 900, 4, 2, 192, seed=7),
     "many_segments_c2": lambda: _many(2),
     "many_segments_c1": lambda: _many(1),
+    # ratio 128, several windows per workgroup (the backward's copy ring in
+    # its steady state) with segment tails and padding rows
+    "long_r128_c2": lambda: inputs.custom("l2", [15000, 2049, 40000, 777, 30000], 88400, 128, 2, 64, seed=8),
+    "long_r128_c1": lambda: inputs.custom("l1", [33333, 129, 20000, 4095], 57900, 128, 1, 128, seed=9),
 }
 
 
