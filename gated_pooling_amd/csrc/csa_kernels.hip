@@ -494,17 +494,53 @@ __device__ __forceinline__ void fetch_window(Window<R, CO, C, BWD>& w, uint32_t 
 // offset plus a uniform row offset.  Masked loads use a uniform offset at
 // the end of the buffer (the host keeps end + row bytes below 2^32).
 // ---------------------------------------------------------------------------
+// The segment table of a pack of fewer than 64 segments, held in registers:
+// lane i of `cu` / `off` holds cu_seqlens[i] / the output-block offset of
+// segment i (i <= S).  The uniform kernels build it per wave from the device
+// cu_seqlens with one load and a wave prefix sum (no LDS, no barrier) and
+// read entries with v_readlane.
+struct RegTable {
+  int32_t cu, off;
+  bool on;
+};
+
+// Builds the register table; returns true (uniformly across the wave) iff cu
+// is a valid pack for (S, T_cap, N), with the checks of load_segment_table.
+template <int R>
+__device__ __forceinline__ bool reg_segment_table(const SegParams& sp, RegTable& rt) {
+  const int S = sp.S, lane = static_cast<int>(threadIdx.x & 63);
+  const int32_t c = lane <= S ? sp.cu[lane] : 0;
+  const int32_t L = __shfl_down(c, 1, 64) - c;                  // lane < S: segment length
+  const int32_t nb = (lane < S && L > 0) ? L / R : 0;
+  int32_t incl = nb;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  const bool bad_len = lane < S && L < 0;
+  const int32_t total = __builtin_amdgcn_readlane(incl, S);
+  const int32_t c0 = __builtin_amdgcn_readlane(c, 0), cS = __builtin_amdgcn_readlane(c, S);
+  rt.cu = c;
+  rt.off = incl - nb;  // exclusive prefix; lane S: the total
+  rt.on = true;
+  return __ballot(bad_len) == 0 && c0 == 0 && static_cast<int64_t>(cS) <= sp.T_cap && total == sp.N;
+}
+
 template <int TBL>
 struct UTable {
   const SegParams& sp;   // kTableArgs: entries straight from the kernel arguments
   const int32_t* cu;     // otherwise: the table in LDS or in the workspace
   const int32_t* off;
+  RegTable rt{0, 0, false};  // kTableLds with fewer than 64 segments: in registers
   __device__ __forceinline__ uint32_t cu_at(int i) const {
     if constexpr (TBL == kTableArgs) return static_cast<uint32_t>(sp.arg_cu[i]);
+    else if (TBL == kTableLds && rt.on) return static_cast<uint32_t>(__builtin_amdgcn_readlane(rt.cu, i));
     else return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(cu[i]));
   }
   __device__ __forceinline__ uint32_t off_at(int i) const {
     if constexpr (TBL == kTableArgs) return static_cast<uint32_t>(sp.arg_off[i]);
+    else if (TBL == kTableLds && rt.on) return static_cast<uint32_t>(__builtin_amdgcn_readlane(rt.off, i));
     else return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(off[i]));
   }
 };
@@ -632,8 +668,16 @@ template <int R, int CO, int C, int NT, int TBL, bool UNI, int PF, bool PAD>
 __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
   extern __shared__ int32_t lds[];
   SegTable tab{nullptr, nullptr};
-  // the uniform path reads a kernel-argument table directly: no LDS copy
-  if constexpr (!(UNI && TBL == kTableArgs)) {
+  RegTable rt{0, 0, false};
+  // the uniform path reads a kernel-argument table directly (no LDS copy) and
+  // keeps a device table of fewer than 64 segments in registers
+  if constexpr (UNI && TBL == kTableLds) {
+    if (p.seg.S < 64) {
+      if (!reg_segment_table<R>(p.seg, rt)) return;
+    } else if (!load_segment_table<R, NT, TBL>(p.seg, lds, tab)) {
+      return;
+    }
+  } else if constexpr (!(UNI && TBL == kTableArgs)) {
     if (!load_segment_table<R, NT, TBL>(p.seg, lds, tab)) return;
   }
 
@@ -664,7 +708,7 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
     for (int i = 0; i < R; ++i) load_f32<C>(rape, active ? (i * W + h * d + g * C) * 4u : R * W * 4u, ape_r[h][i]);
 
   if constexpr (UNI) {
-    const UTable<TBL> t{p.seg, tab.cu, tab.off};
+    const UTable<TBL> t{p.seg, tab.cu, tab.off, rt};
     WinCtxU x;
     x.S = p.seg.S;
     x.N = N;
@@ -790,11 +834,16 @@ template <int R, int CO, int C, int NT, int TBL, bool UNI, int PF, bool PAD>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   extern __shared__ int32_t lds[];
   SegTable tab{nullptr, nullptr};
+  RegTable rt{0, 0, false};
   bool valid = true;
-  // the uniform path reads a kernel-argument table directly (no LDS copy);
-  // the zero-fill workgroups still walk it from LDS
+  // the uniform path reads a kernel-argument table directly (no LDS copy) and
+  // keeps a device table of fewer than 64 segments in registers; the
+  // zero-fill workgroups still walk the table from LDS
   if constexpr (UNI && TBL == kTableArgs) {
     if (blockIdx.x >= p.main_wgs) load_segment_table<R, NT, TBL>(p.seg, lds, tab);
+  } else if constexpr (UNI && TBL == kTableLds) {
+    if (blockIdx.x >= p.main_wgs || p.seg.S >= 64) valid = load_segment_table<R, NT, TBL>(p.seg, lds, tab);
+    else valid = reg_segment_table<R>(p.seg, rt);
   } else {
     valid = load_segment_table<R, NT, TBL>(p.seg, lds, tab);
   }
@@ -977,7 +1026,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   if constexpr (UNI) {
     // CS >= 64: the lanes of a wave share one row
     n = __builtin_amdgcn_readfirstlane(n);
-    const UTable<TBL> t{p.seg, tab.cu, tab.off};
+    const UTable<TBL> t{p.seg, tab.cu, tab.off, rt};
     WinCtxU x;
     x.S = p.seg.S;
     x.N = N;
