@@ -215,9 +215,9 @@ int64_t pow2_floor(int64_t x) {
 
 // ratio 128: a workgroup per (column slice, group of output rows), rows of a
 // slice dealt round-robin to its workgroups (see the kernels).
-//   forward: two waves per 64-entry chunk, the staged window and two exchange
-//     sets in dynamic LDS after the segment table; two workgroups per CU at
-//     coff 2, four at coff 1 (measured best on 65536-token packs);
+//   forward: 4 * coff waves per workgroup, two half-window stages and the
+//     exchange area in dynamic LDS after the segment table; two workgroups
+//     per CU at coff 2, four at coff 1 (measured best on 65536-token packs);
 //   backward: 1024 threads, one workgroup per CU (its two static LDS window
 //     buffers take most of the CU's LDS); every workgroup also zero-fills a
 //     share of the never-read rows after its windows, so there are no
@@ -243,18 +243,14 @@ Plan make_plan_r128(const Problem& p) {
     return per;
   };
   {
-    const int rows = p.coff * csa::kRatio128;           // window rows
-    const int chunks = rows / csa::kChunk128;
-    const int NT = 2 * chunks * 64;                      // two waves per 64-entry chunk
-    // two exchange sets: wave maxima, part-0 chains, chunk sums
-    const uint64_t red_bytes = 2ull * (2 * chunks * 64 + 4 * chunks * 64) * 4;
-    const uint64_t stage_bytes = 2ull * rows * csa::kSlice128 * 2;   // staged window (score, kv)
+    const int NT = csa::fwd128_threads(p.coff);
     const int64_t per = per_slice(tu.r128_fwd_wgs ? tu.r128_fwd_wgs : (p.coff == 2 ? 2 : 4) * csa::kCUs);
     pl.fwd.grid = static_cast<uint32_t>(per * pl.nslices);
     pl.fwd.threads = NT;
     pl.fwd.cols = 1;
     pl.fwd_lds_table_words = table_words(NT);
-    pl.fwd.lds_bytes = pl.fwd_lds_table_words * 4ull + stage_bytes + red_bytes;
+    pl.fwd.lds_bytes = pl.fwd_lds_table_words * 4ull + csa::fwd128_stage_bytes(p.coff) +
+                       csa::fwd128_red_bytes(p.coff);
     pl.ws_fwd = pl.global_table ? kHeaderBytes + pl.off_bytes : 0;
   }
   {

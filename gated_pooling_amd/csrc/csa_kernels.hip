@@ -1203,23 +1203,25 @@ __global__ __launch_bounds__(kReduceNT) void dape_reduce_kernel(ReduceParams p) 
 // column, too many for one lane's registers, so both kernels stage windows in
 // LDS: a workgroup owns a slice of kSlice128 = 64 columns (lane = column) and
 // walks output rows.  Each lane's window entries are split over the waves
-// (one per 32 entries in the forward, per 8 coff entries in the backward),
-// and per row:
+// (16 per wave and half window in the forward, 8 coff per wave in the
+// backward), and per row:
 //   1. x = score + ape for the wave's entries, the wave's max, exchanged
-//      through LDS -> window max m;
+//      through LDS -> the window max m (backward) or the max of each half
+//      window (forward);
 //   2. e = EXP(x - m); the entries' Z (adds) and acc (fma chain from 0) are
-//      summed in an order fixed per kernel (below), chains of consecutive
-//      entries first, then the chain sums in window order;
+//      summed in chains of consecutive entries, then the chain sums in window
+//      order; the forward merges its two halves by rescaling with EXP of the
+//      difference of their maxima;
 //   forward 3. out = acc * (1/Z) as bf16;
 //   backward 3. a = e R g, ds = a (v - o) as bf16, written over the staged
 //      inputs in LDS and stored with 16-byte stores; dAPE sums stay in
 //      registers (a wave always holds the same positions of its slice) and
 //      leave as one partial row per workgroup.
-// These summation orders are not the single chain of the ratio 2 and 4
-// kernels: the pages hold ratio 128 to the final bf16 rounding instead of to
-// bit equality [PR5984: ratio=128 commit, numerics contract per ratio family],
-// and include/csa.h states the bound.  head_dim is a multiple of kSlice128,
-// so every slice is whole.
+// These orders are not the single chain of the ratio 2 and 4 kernels: the
+// pages hold ratio 128 to the final bf16 rounding instead of to bit equality
+// [PR5984: ratio=128 commit, numerics contract per ratio family], and
+// include/csa.h states the bound.  head_dim is a multiple of kSlice128, so
+// every slice is whole.
 // ---------------------------------------------------------------------------
 
 // Byte offset in kv/score of window row k's slice, or `oob` when the row is
@@ -1260,210 +1262,214 @@ __device__ __forceinline__ Row128 row128(uint32_t n, uint32_t N, int& s_hint, co
   return r;
 }
 
-// Forward: two workgroups per CU (a 64 KB staged window each), each 2 waves
-// per 64-entry chunk (32 entries per wave, `part` 0 and 1): part 0 starts the
-// chunk's Z and acc chains, part 1 continues them (handed over through LDS),
-// then the chunk sums are added in chunk order.  The window slices are loaded
-// with 16-byte loads into registers one row ahead and written to LDS while
-// the previous row has finished, so each workgroup keeps one window of loads
-// in flight while it computes, two per CU.
+// Forward: two workgroups per CU at coff 2 (four at coff 1), 4 * coff waves
+// each.  A window is computed in two halves of kRows / 2 rows (coff 2: the
+// previous block's rows, then the block's own rows; coff 1: the first and the
+// last 64 rows), each half with its own maximum, and the halves are merged by
+// rescaling, as the pages' forward merges per-chunk partials that carry their
+// own maxima [PR5984: ratio=128 commit].  Per half h: m_h = max x over the
+// half, e = EXP(x - m_h), Z_h and A_h the sums of e and e v (each wave a chain
+// over its 16 entries, the wave sums added in wave order); then
+// M = max(m_0, m_1), Z = Z_0 EXP(m_0 - M) + Z_1 EXP(m_1 - M), A likewise, and
+// out = A (1/Z).  Halves are loaded with 16-byte loads into one of two
+// register slots two halves ahead and written to one of two LDS stages while
+// the previous half computes, so each workgroup keeps a window of loads in
+// flight and a window's first half computes while its second half is still
+// arriving.
 template <int CO>
-struct Win128 {
-  static constexpr int kRows = CO * kRatio128;        // window rows
-  static constexpr int kChunks = kRows / kChunk128;   // summation chunks
-  static constexpr int kPart = kChunk128 / 2;         // entries per wave
-  static constexpr int kWaves = 2 * kChunks;
-  static constexpr int kThreads = kWaves * 64;
-  static constexpr int kStageBytes = 2 * kRows * kSlice128 * 2;  // score, kv as bf16
-  // one exchange set: wave maxima [kWaves][64], part-0 chains [2][kChunks][64],
-  // chunk sums [2][kChunks][64]
-  static constexpr int kRedFloats = kWaves * 64 + 4 * kChunks * 64;
+struct F128 {
+  static constexpr int kRows = CO * kRatio128;              // window rows
+  static constexpr int kHalfRows = kRows / 2;               // rows of a half window
+  static constexpr int kWaves = fwd128_threads(CO) / 64;
+  static constexpr int kThreads = fwd128_threads(CO);
+  static constexpr int kE = kHalfRows / kWaves;             // entries per lane and half
+  static constexpr int kParts = kSlice128 * 2 / 16;         // 16-byte parts of a row slice
+  static constexpr int kIters = 2 * kHalfRows * kParts / kThreads;  // a thread's loads per half
+  static constexpr int kRowsPerIter = kThreads / kParts;
+  static constexpr int kHalfBytes = 2 * kHalfRows * kSlice128 * 2;  // score rows, then kv rows
+  static_assert(2 * kHalfRows * kParts % kThreads == 0 && kIters % 2 == 0, "whole iterations");
+  static_assert(2 * kHalfBytes == fwd128_stage_bytes(CO), "two stages");
+  static_assert(3 * kWaves * kSlice128 * 4 == fwd128_red_bytes(CO), "exchange area");
 };
 
-// Byte offset in kv/score of window row k's slice, or `oob` when the row is
-// masked (the previous half of a segment's first block).
-// A thread's share of one staged window: kIters 16-byte parts; iterations
-// [0, kIters/2) are score rows, the rest kv rows, so the buffer resource of
+// A thread's share of one half window, in registers.
+template <int CO>
+struct Half128 {
+  u32x4 v[F128<CO>::kIters];
+};
+
+// Row of the half read by iteration it of this thread: iterations
+// [0, kIters / 2) are score rows, the rest kv rows, so the buffer resource of
 // each load is known at compile time.
 template <int CO>
-struct Stage128 {
-  static constexpr int kParts = kSlice128 * 2 / 16;  // 16-byte parts of a row slice
-  static constexpr int kIters = 2 * Win128<CO>::kRows * kParts / Win128<CO>::kThreads;
-  static constexpr int kRowsPerIter = Win128<CO>::kThreads / kParts;
-  static_assert(2 * Win128<CO>::kRows * kParts % Win128<CO>::kThreads == 0, "whole iterations");
-  u32x4 v[kIters];
-  // window row and tensor of iteration it for this thread
-  __device__ static __forceinline__ int row_of(int it) {
-    return static_cast<int>(threadIdx.x / kParts) + (it % (kIters / 2)) * kRowsPerIter;
-  }
-};
+__device__ __forceinline__ int half_row128(int it) {
+  using F = F128<CO>;
+  return static_cast<int>(threadIdx.x / F::kParts) + (it % (F::kIters / 2)) * F::kRowsPerIter;
+}
 
-// Issue every load of a thread's share of the window (no wait).
+// Issue the loads of half h of row's window (no wait).  Rows past the pack
+// and masked rows load from past the buffer's range and read zeros; every
+// call issues the same loads, so the compiler's waits count a fixed number of
+// loads between two halves.
 template <int CO>
-__device__ __forceinline__ void issue_window128(Stage128<CO>& st, rsrc_t rsc, rsrc_t rkv, const Row128& row,
-                                                uint32_t row_bytes, uint32_t half_bytes, uint32_t slice_bytes,
-                                                uint32_t oob) {
-  using S = Stage128<CO>;
-  const uint32_t part = threadIdx.x % S::kParts;
+__device__ __forceinline__ void issue_half128(Half128<CO>& hv, rsrc_t rsc, rsrc_t rkv, const Row128& row, int h,
+                                              uint32_t row_bytes, uint32_t half_bytes, uint32_t slice_bytes,
+                                              uint32_t oob) {
+  using F = F128<CO>;
+  const uint32_t part = threadIdx.x % F::kParts;
 #pragma unroll
-  for (int it = 0; it < S::kIters; ++it) {
-    const uint32_t o = row128_offset<CO>(S::row_of(it), row.own, CO == 2 && row.has_prev, row_bytes, half_bytes,
-                                         slice_bytes, oob);
-    st.v[it] = __builtin_amdgcn_raw_buffer_load_b128(it < S::kIters / 2 ? rsc : rkv, o == oob ? oob : o + part * 16u,
+  for (int it = 0; it < F::kIters; ++it) {
+    const uint32_t o = row.valid ? row128_offset<CO>(h * F::kHalfRows + half_row128<CO>(it), row.own,
+                                                     CO == 2 && row.has_prev, row_bytes, half_bytes, slice_bytes, oob)
+                                 : oob;
+    hv.v[it] = __builtin_amdgcn_raw_buffer_load_b128(it < F::kIters / 2 ? rsc : rkv, o == oob ? oob : o + part * 16u,
                                                      0, kAuxStream);
   }
 }
 
-// Write a thread's share of the window into LDS (waits for its loads).
+// Write a thread's share of a half into an LDS stage (waits for its loads).
 template <int CO>
-__device__ __forceinline__ void write_window128(uint16_t* stage, const Stage128<CO>& st) {
-  using S = Stage128<CO>;
-  const int part = threadIdx.x % S::kParts;
+__device__ __forceinline__ void write_half128(uint16_t* st, const Half128<CO>& hv) {
+  using F = F128<CO>;
+  const int part = threadIdx.x % F::kParts;
 #pragma unroll
-  for (int it = 0; it < S::kIters; ++it) {
-    const int rq = (it / (S::kIters / 2)) * Win128<CO>::kRows + S::row_of(it);
-    *reinterpret_cast<u32x4*>(stage + rq * kSlice128 + part * 8) = st.v[it];
+  for (int it = 0; it < F::kIters; ++it) {
+    const int rq = (it / (F::kIters / 2)) * F::kHalfRows + half_row128<CO>(it);
+    *reinterpret_cast<u32x4*>(st + rq * kSlice128 + part * 8) = hv.v[it];
   }
 }
 
-// A wave's place in the window: chunk, part, half and first block position.
-template <int CO>
-struct Wave128 {
-  int chunk, part, half;
-  uint32_t pos0;        // block position of the wave's first entry
-  uint32_t k0;          // window row of the wave's first entry
-  __device__ __forceinline__ explicit Wave128(int wave) {
-    chunk = wave >> 1;
-    part = wave & 1;
-    half = (CO == 2) ? (chunk >> 1) : 0;
-    pos0 = (chunk & 1) * kChunk128 + part * Win128<CO>::kPart;
-    k0 = half * kRatio128 + pos0;
-  }
-  // the previous-half waves of a segment's first block have no entries
-  __device__ __forceinline__ bool present(const Row128& row) const { return !(CO == 2 && half == 0 && !row.has_prev); }
-};
-
-// Window max and chunk sums through one exchange set.  x holds the wave's
-// logits on entry and its e = EXP(x - m) on return; sv points at the wave's
-// first staged kv entry (stride kSlice128); Z/acc are the window's.
-template <int CO>
-__device__ __forceinline__ void softmax128(float (&x)[Win128<CO>::kPart], const uint16_t* sv, bool present,
-                                           bool has_prev, int wave, int lane, const Wave128<CO>& wv, float* red,
-                                           float& Z, float& acc) {
-  using Wn = Win128<CO>;
-  constexpr int K = Wn::kPart;
-  float* rm = red;                                  // [kWaves][64]
-  float* rz0 = red + Wn::kWaves * 64;               // [kChunks][64] part-0 Z
-  float* ra0 = rz0 + Wn::kChunks * 64;              // [kChunks][64] part-0 acc
-  float* rz = ra0 + Wn::kChunks * 64;               // [kChunks][64] chunk Z
-  float* ra = rz + Wn::kChunks * 64;                // [kChunks][64] chunk acc
-  const int first_w = (CO == 2 && !has_prev) ? Wn::kWaves / 2 : 0;
+// One half from stage st (present is uniform across the workgroup): the
+// wave's x = score + APE and its max into red; after a barrier, `mid` (the
+// next half's LDS write and the loads after it), the half's max m, e =
+// EXP(x - m) and the wave's Z and acc chains into red; after a second barrier
+// wave 0 adds the wave sums in wave order into Z and A.  red holds the wave
+// maxima, wave Z and wave acc, [kWaves][64] each.
+template <int CO, typename Mid>
+__device__ __forceinline__ void half128(const uint16_t* st, const float (&ape)[F128<CO>::kE], bool present, int wave,
+                                        int lane, float* red, Mid&& mid, float& m, float& Z, float& A) {
+  using F = F128<CO>;
+  constexpr int E = F::kE, NW = F::kWaves, NC = kSlice128;
+  const uint16_t* ss = st + wave * E * NC + lane;
+  const uint16_t* sv = st + (F::kHalfRows + wave * E) * NC + lane;
+  float x[E];
   if (present) {
-    float m = x[0];
 #pragma unroll
-    for (int k = 1; k < K; ++k) m = fmaxf(m, x[k]);
-    rm[wave * 64 + lane] = m;
+    for (int e = 0; e < E; ++e) x[e] = __uint_as_float(uint32_t(ss[e * NC]) << 16) + ape[e];
+    float mw = x[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) mw = fmaxf(mw, x[e]);
+    red[wave * NC + lane] = mw;
   }
   __syncthreads();
-  float m = rm[first_w * 64 + lane];
-  for (int w = first_w + 1; w < Wn::kWaves; ++w) m = fmaxf(m, rm[w * 64 + lane]);
+  mid();
   if (present) {
+    m = red[lane];
 #pragma unroll
-    for (int k = 0; k < K; ++k) x[k] = csa_exp(x[k] - m);
-    if (wv.part == 0) {
-      float zc = x[0], ac = 0.0f;
+    for (int w = 1; w < NW; ++w) m = fmaxf(m, red[w * NC + lane]);
 #pragma unroll
-      for (int k = 1; k < K; ++k) zc = zc + x[k];
+    for (int e = 0; e < E; ++e) x[e] = csa_exp(x[e] - m);
+    float zl = x[0], al = 0.0f;
 #pragma unroll
-      for (int k = 0; k < K; ++k) ac = __builtin_fmaf(x[k], __uint_as_float(uint32_t(sv[k * kSlice128]) << 16), ac);
-      rz0[wv.chunk * 64 + lane] = zc;
-      ra0[wv.chunk * 64 + lane] = ac;
+    for (int e = 1; e < E; ++e) zl = zl + x[e];
+#pragma unroll
+    for (int e = 0; e < E; ++e) al = __builtin_fmaf(x[e], __uint_as_float(uint32_t(sv[e * NC]) << 16), al);
+    red[(NW + wave) * NC + lane] = zl;
+    red[(2 * NW + wave) * NC + lane] = al;
+  }
+  __syncthreads();
+  if (present && wave == 0) {
+    Z = red[NW * NC + lane];
+    A = red[2 * NW * NC + lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      Z = Z + red[(NW + w) * NC + lane];
+      A = A + red[(2 * NW + w) * NC + lane];
     }
-  }
-  __syncthreads();
-  if (present && wv.part == 1) {
-    float zc = rz0[wv.chunk * 64 + lane], ac = ra0[wv.chunk * 64 + lane];
-#pragma unroll
-    for (int k = 0; k < K; ++k) zc = zc + x[k];
-#pragma unroll
-    for (int k = 0; k < K; ++k) ac = __builtin_fmaf(x[k], __uint_as_float(uint32_t(sv[k * kSlice128]) << 16), ac);
-    rz[wv.chunk * 64 + lane] = zc;
-    ra[wv.chunk * 64 + lane] = ac;
-  }
-  __syncthreads();
-  const int first_c = first_w / 2;
-  Z = rz[first_c * 64 + lane];
-  acc = ra[first_c * 64 + lane];
-  for (int c = first_c + 1; c < Wn::kChunks; ++c) {
-    Z = Z + rz[c * 64 + lane];
-    acc = acc + ra[c * 64 + lane];
   }
 }
 
 template <int CO, int TBL>
-__global__ __launch_bounds__(Win128<CO>::kThreads) void fwd128_kernel(Fwd128Params p) {
-  using Wn = Win128<CO>;
-  constexpr int NT = Wn::kThreads, K = Wn::kPart;
+__global__ __launch_bounds__(F128<CO>::kThreads) void fwd128_kernel(Fwd128Params p) {
+  using F = F128<CO>;
+  constexpr int NT = F::kThreads, E = F::kE, NC = kSlice128;
   extern __shared__ int32_t lds[];
   SegTable tab{nullptr, nullptr};
   if constexpr (TBL != kTableArgs) {
     if (!load_segment_table<kRatio128, NT, TBL>(p.seg, lds, tab)) return;
   }
-  // LDS: [table][staged window][two exchange sets]
-  uint16_t* stage = reinterpret_cast<uint16_t*>(lds + p.lds_table_words);
-  float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(stage) + Wn::kStageBytes);
+  // LDS: [table][two half-window stages][exchange]
+  uint16_t* stage0 = reinterpret_cast<uint16_t*>(lds + p.lds_table_words);
+  uint16_t* stage1 = stage0 + F::kHalfBytes / 2;
+  float* red = reinterpret_cast<float*>(stage0 + F::kHalfBytes);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const Wave128<CO> wv(wave);
   const uint32_t d = p.head_dim, W = CO * d, N = static_cast<uint32_t>(p.seg.N);
   const uint32_t nslices = p.nslices, slice = blockIdx.x % nslices, per_slice = gridDim.x / nslices;
-  const uint32_t col = slice * kSlice128 + lane;
+  const uint32_t col = slice * NC + lane;
   const rsrc_t rkv = make_rsrc(p.kv, p.io_bytes);
   const rsrc_t rsc = make_rsrc(p.score, p.io_bytes);
   const rsrc_t rape = make_rsrc(p.ape, kRatio128 * W * 4u);
   const rsrc_t rout = make_rsrc(p.out, N * d * 2u);
-  const uint32_t ape_off = (wv.pos0 * W + wv.half * d + col) * 4u;
-  float ape_r[K];
+  // APE of the wave's entries: window row k = h kHalfRows + kE wave + e is
+  // block position k mod 128 of the window's column half k / 128
+  float ape_r[2][E];
 #pragma unroll
-  for (int k = 0; k < K; ++k)
-    ape_r[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rape, ape_off, k * W * 4u, 0));
-  const uint16_t* ss = stage + wv.k0 * kSlice128 + lane;
-  const uint16_t* sv = stage + (Wn::kRows + wv.k0) * kSlice128 + lane;
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t k = h * F::kHalfRows + wave * E + e;
+      ape_r[h][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rape, ((k % kRatio128) * W + (CO == 2 ? k / kRatio128 : 0u) * d + col) * 4u, 0, 0));
+    }
 
   const UTable<TBL> t{p.seg, tab.cu, tab.off};
   int s_hint = 0;
-  const uint32_t row_bytes = W * 2u, half_bytes = d * 2u, slice_bytes = slice * kSlice128 * 2u;
-  // The next row's window is loaded into registers while this row computes.
-  Stage128<CO> st;
+  const uint32_t row_bytes = W * 2u, half_bytes = d * 2u, slice_bytes = slice * NC * 2u, oob = p.io_bytes;
   uint32_t n = __builtin_amdgcn_readfirstlane(blockIdx.x / nslices);
-  Row128 row{};
-  if (n < N) {
-    row = row128<TBL>(n, N, s_hint, t, p.seg.S);
-    issue_window128<CO>(st, rsc, rkv, row, row_bytes, half_bytes, slice_bytes, p.io_bytes);
-  }
-  uint32_t set = 0;
-  for (; n < N; n += per_slice, set ^= 1u) {
-    write_window128<CO>(stage, st);
-    __syncthreads();
-    const uint32_t nn = n + per_slice;
-    Row128 nrow{};
-    if (nn < N) {
-      nrow = row128<TBL>(nn, N, s_hint, t, p.seg.S);
-      issue_window128<CO>(st, rsc, rkv, nrow, row_bytes, half_bytes, slice_bytes, p.io_bytes);
-    }
-    const bool present = wv.present(row);
-    float x[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) x[k] = __uint_as_float(uint32_t(ss[k * kSlice128]) << 16) + ape_r[k];
-    float Z, acc;
-    // every read of the staged window happens before softmax128's last barrier
-    softmax128<CO>(x, sv, present, row.has_prev, wave, lane, wv, red + set * Wn::kRedFloats, Z, acc);
+  if (n >= N) return;
+  // Slot h0 holds first halves, h1 second halves; r0, r1, r2: this row and
+  // the next two of the workgroup
+  Row128 r0 = row128<TBL>(n, N, s_hint, t, p.seg.S);
+  Row128 r1 = row128<TBL>(n + per_slice, N, s_hint, t, p.seg.S);
+  Half128<CO> h0, h1;
+  issue_half128<CO>(h0, rsc, rkv, r0, 0, row_bytes, half_bytes, slice_bytes, oob);
+  issue_half128<CO>(h1, rsc, rkv, r0, 1, row_bytes, half_bytes, slice_bytes, oob);
+  write_half128<CO>(stage0, h0);
+  issue_half128<CO>(h0, rsc, rkv, r1, 0, row_bytes, half_bytes, slice_bytes, oob);
+  __syncthreads();
+  for (;;) {
+    const Row128 r2 = row128<TBL>(n + 2 * per_slice, N, s_hint, t, p.seg.S);
+    float m0 = 0.0f, Z0 = 0.0f, A0 = 0.0f, m1 = 0.0f, Z1 = 0.0f, A1 = 0.0f;
+    // the first half (absent in a segment's first block at coff 2); meanwhile
+    // this row's second half goes to stage 1 and the next row's is loaded
+    const bool first = !(CO == 2 && !r0.has_prev);
+    half128<CO>(stage0, ape_r[0], first, wave, lane, red, [&] {
+      write_half128<CO>(stage1, h1);
+      issue_half128<CO>(h1, rsc, rkv, r1, 1, row_bytes, half_bytes, slice_bytes, oob);
+    }, m0, Z0, A0);
+    // the second half; meanwhile the next row's first half goes to stage 0
+    // and the first half of the row after it is loaded
+    half128<CO>(stage1, ape_r[1], true, wave, lane, red, [&] {
+      write_half128<CO>(stage0, h0);
+      issue_half128<CO>(h0, rsc, rkv, r2, 0, row_bytes, half_bytes, slice_bytes, oob);
+    }, m1, Z1, A1);
     if (wave == 0) {
-      const float o = acc * (1.0f / Z);
+      float Z = Z1, A = A1;
+      if (first) {
+        const float M = fmaxf(m0, m1);
+        const float s0 = csa_exp(m0 - M), s1 = csa_exp(m1 - M);
+        Z = Z0 * s0 + Z1 * s1;
+        A = A0 * s0 + A1 * s1;
+      }
+      const float o = A * (1.0f / Z);
       const Pack<1> ob{{pack_bf16x2(o, 0.0f)}};
       store_pack<1>(rout, (n * d + col) * 2u, ob);
     }
-    row = nrow;
+    n += per_slice;
+    if (n >= N) break;
+    r0 = r1;
+    r1 = r2;
   }
 }
 
@@ -2020,7 +2026,7 @@ bool launch_bwd(int ratio, int coff, const BwdParams& p, const LaunchShape& sh, 
 
 template <int CO>
 static void launch_fwd128_c(const Fwd128Params& p, uint32_t grid, size_t lds_bytes, hipStream_t st) {
-  const dim3 g(grid), b(Win128<CO>::kThreads);
+  const dim3 g(grid), b(F128<CO>::kThreads);
   if (p.seg.table == kTableGlobal)
     hipLaunchKernelGGL((fwd128_kernel<CO, kTableGlobal>), g, b, lds_bytes, st, p);
   else if (p.seg.table == kTableArgs)

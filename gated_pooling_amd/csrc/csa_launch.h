@@ -75,15 +75,19 @@ struct BwdParams {
 
 // ratio = 128 (windows of 128 * coff rows): a workgroup owns a slice of
 // kSlice128 columns (one per lane) and walks output rows; head_dim must be a
-// multiple of kSlice128.  Forward: the window slice is staged in LDS and each
-// summation chunk of kChunk128 entries is held by two waves; two workgroups
-// per CU.  Backward: workgroups of kThreads128 threads, one per CU (grids
-// capped at kCUs), each window copied into one of two static LDS buffers;
-// kRed128Bytes is its dynamic LDS exchange area after the segment table
-// (wave maxima, wave Z, wave acc).
+// multiple of kSlice128.  Forward: workgroups of 4 * coff waves (two per CU
+// at coff 2, four at coff 1) compute a window in two halves of 64 * coff
+// rows, staged in LDS: dynamic LDS = the segment table, two half-window
+// stages (score and kv rows, bf16) and an exchange area of three floats per
+// wave and column (wave maximum, wave Z, wave acc).  Backward: workgroups of
+// kThreads128 threads, one per CU (grids capped at kCUs), each window copied
+// into one of two static LDS buffers; kRed128Bytes is its dynamic LDS
+// exchange area after the segment table (wave maxima, wave Z, wave acc).
 constexpr int kRatio128 = 128;
 constexpr int kSlice128 = 64;
-constexpr int kChunk128 = 64;
+constexpr int fwd128_threads(int coff) { return 4 * coff * 64; }
+constexpr int fwd128_stage_bytes(int coff) { return 2 * (2 * 64 * coff * kSlice128 * 2); }
+constexpr int fwd128_red_bytes(int coff) { return 3 * 4 * coff * kSlice128 * 4; }
 constexpr int kThreads128 = 1024;
 constexpr int kRed128Bytes = 3 * (kThreads128 / 64) * kSlice128 * 4;
 constexpr int kCUs = 256;  // MI355X

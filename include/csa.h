@@ -34,14 +34,18 @@
  *   from 0;  o = acc*R;  out = bf16_rne(o);  backward: G = R*f32(dout),
  *   a = e*G, dkv = bf16_rne(a), ds = a*(v - o), dscore = bf16_rne(ds).
  *   At ratio 2 and 4 the kernels evaluate exactly this order.  At ratio 128
- *   (windows of 128 or 256 entries) they sum Z and acc in chains of
- *   consecutive entries in this order (the forward: chunks of 64 entries;
- *   the backward: 8 * coff entries) and then add the chain sums in window
- *   order ([PR5984: ratio=128 commit]: per-chunk partials merged in one fixed
- *   order), which is still fixed (bit-identical run to run) but differs from
- *   the single chain above by the rounding of the reordered sums: out, dkv
+ *   (windows of 128 or 256 entries) the backward sums Z and acc in chains of
+ *   8 * coff consecutive entries and adds the chain sums in window order; the
+ *   forward evaluates each half window (coff 2: the previous block's rows,
+ *   then the own rows; coff 1: 64 rows each) with its own maximum m_h, sums
+ *   16-entry chains of EXP(x - m_h) the same way and merges the halves as
+ *   Z = Z_0 EXP(m_0 - M) + Z_1 EXP(m_1 - M), acc likewise, M the larger
+ *   maximum ([PR5984: ratio=128 commit]: per-chunk partials with their own
+ *   maxima, merged in one fixed order).  Both orders are fixed (bit-identical
+ *   run to run) but differ from the single chain above by rounding: out, dkv
  *   within one bf16 ulp of the single-chain result or the error bound of the
- *   reordering, dscore likewise, dape within 1e-5 of its largest magnitude.
+ *   reordering and rescaling, dscore likewise, dape within 1e-5 of its
+ *   largest magnitude.
  *   EXP(y) = ldexp(P7(r), k) with y clamped to >= -104, k = rint(y*log2 e),
  *   r = y - k*ln2 in two fma steps, P7 the degree-7 Taylor polynomial of
  *   e^r (coefficients fp32(1/n!)), within 1 fp32 ulp of e^y over [-104, 0];

@@ -4,9 +4,10 @@ Contract (checked element by element on seeded inputs):
   * ratio 2 and 4: out, dKV, dScore bit-identical to the oracle's fp32
     evaluation order (the stated tolerance is 1 bf16 ulp; both sides evaluate
     the same fixed fp32 order, so the expected difference is none);
-  * ratio 128: the kernels sum each window in 64-entry chunks, the oracle in
-    one chain, so results are compared within 1 bf16 ulp or the error bound
-    of that reordering, with the pages' ratio-128 gate as a floor
+  * ratio 128: the kernels sum each window in chains (the forward by half
+    windows with their own maxima, merged by rescaling), the oracle in one
+    chain, so results are compared within 1 bf16 ulp or the error bound of
+    that reordering, with the pages' ratio-128 gate as a floor
     (tests/tolerance.py);
   * never-consumed dKV/dScore slots: exactly 0x0000 although the output
     buffers were filled with NaN before the call;
@@ -308,13 +309,19 @@ def _r128_cases():
         lengths = rng.integers(1000, 9000, size=nseg).tolist()
         T = int(sum(lengths)) + int(rng.integers(1, 500))
         cases.append((lengths, T, c, d, 960 + i, bool(i % 2)))
+    # the largest segment table kept in LDS (2048 segments) at coff 2: the
+    # backward's two window buffers plus the table use nearly all of a CU's
+    # 160 KiB of LDS
+    lengths = np.random.default_rng(2048).integers(0, 300, size=2048).tolist()
+    cases.append((lengths, int(sum(lengths)) + 5, 2, 64, 970, False))
     return cases
 
 
 @pytest.mark.parametrize("case", _r128_cases(), ids=lambda c: f"S{len(c[0])}_c{c[2]}_d{c[3]}_s{c[4]}")
 def test_ratio128_packs(dev, case):
     """ratio 128: windows of 128 * coff rows staged through LDS, summed in
-    64-entry chunks (compared within the reordering tolerance); multi-block
+    chains (the forward by half windows with their own maxima), compared
+    within the reordering tolerance; multi-block
     segments, tails, segments shorter than 128, padding, kernel-argument /
     LDS / workspace segment tables."""
     lengths, T, c, d, seed, host = case

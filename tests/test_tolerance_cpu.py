@@ -1,11 +1,15 @@
 """Pins for the ratio-128 tolerance checker (tests/tolerance.py), on the CPU.
 
-A numpy model of a reordered evaluation -- every window's Z and acc summed in
-64-entry chunks whose sums are then added in chunk order, the order of the
-ratio-128 kernels -- must pass the checker against the oracle's single-chain
-results; a planted 2-ulp error in any output, a lost zero and a wrong dAPE
-must fail it.  The model is test-side only (it uses the oracle's exponential
-so that only the summation order differs).
+A numpy model of the ratio-128 kernels' evaluation order must pass the
+checker against the oracle's single-chain results: the forward takes each
+half window (coff 2: the previous block's rows, then the own rows; coff 1:
+the first and the last 64 rows) with its own maximum, sums 16-entry chains
+added in chain order, and merges the halves by rescaling with EXP of the
+difference of their maxima; the backward takes the window maximum and sums
+8 * coff-entry chains added in chain order.  A planted 2-ulp error in any
+output, a lost zero and a wrong dAPE must fail the checker.  The model is
+test-side only (it uses the oracle's exponential, so that only the order of
+evaluation differs).
 """
 from __future__ import annotations
 
@@ -15,9 +19,6 @@ import pytest
 import oracle
 from tests import brute
 from tests.tolerance import check_reordered
-
-CHUNK = 64
-
 
 def _bf16(x):
     u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
@@ -34,7 +35,25 @@ def _fma32(a, b, c):
     return np.float32(np.float64(a) * np.float64(b) + np.float64(c))
 
 
-def chunked_model(kv, sc, ape, dout, cu, T, r, c, d):
+def _chains(e, v, L):
+    """Z and acc of chains of L consecutive entries, the chain sums added in
+    chain order."""
+    Z = acc = None
+    for c0 in range(0, len(e), L):
+        zc, ac = e[c0], np.float32(0)
+        for k in range(c0 + 1, min(c0 + L, len(e))):
+            zc = np.float32(zc + e[k])
+        for k in range(c0, min(c0 + L, len(e))):
+            ac = _fma32(e[k], v[k], ac)
+        Z, acc = (zc, ac) if Z is None else (np.float32(Z + zc), np.float32(acc + ac))
+    return Z, acc
+
+
+def _exp(y):
+    return oracle.exp_f32_array(np.asarray([y], np.float32))[0]
+
+
+def kernel_order_model(kv, sc, ape, dout, cu, T, r, c, d):
     W = c * d
     N = brute.count_outputs(cu, r)
     out = np.zeros((N, d), np.uint16)
@@ -48,19 +67,32 @@ def chunked_model(kv, sc, ape, dout, cu, T, r, c, d):
         x = np.array([np.float32(_f(sc[t, col])) + np.float32(ape[pos, col]) for t, col, pos in members],
                      np.float32)
         v = np.array([_f(kv[t, col]) for t, col, _ in members], np.float32)
+        # forward: half windows with their own maxima, merged by rescaling
+        if c == 2:
+            cut = sum(1 for _, col, _ in members if col < d)   # the previous block's rows (0 or 128)
+        else:
+            cut = len(members) // 2
+        parts = []
+        for lo, hi in ((0, cut), (cut, len(members))):
+            if hi > lo:
+                mh = x[lo:hi].max()
+                eh = oracle.exp_f32_array((x[lo:hi] - mh).astype(np.float32))
+                parts.append((mh,) + _chains(eh, v[lo:hi], 16))
+        if len(parts) == 1:
+            _, Zf, Af = parts[0]
+        else:
+            (m0, Z0, A0), (m1, Z1, A1) = parts
+            M = max(m0, m1)
+            s0, s1 = _exp(np.float32(m0 - M)), _exp(np.float32(m1 - M))
+            Zf = np.float32(np.float32(Z0 * s0) + np.float32(Z1 * s1))
+            Af = np.float32(np.float32(A0 * s0) + np.float32(A1 * s1))
+        out[n, j] = _bf16(np.float32(Af * (np.float32(1) / Zf)))
+        # backward: the window maximum, 8 * coff-entry chains
         m = x.max()
         e = oracle.exp_f32_array((x - m).astype(np.float32))
-        Z = acc = np.float32(0)
-        for c0 in range(0, len(e), CHUNK):
-            zc, ac = e[c0], np.float32(0)
-            for k in range(c0 + 1, min(c0 + CHUNK, len(e))):
-                zc = np.float32(zc + e[k])
-            for k in range(c0, min(c0 + CHUNK, len(e))):
-                ac = _fma32(e[k], v[k], ac)
-            Z, acc = (zc, ac) if c0 == 0 else (np.float32(Z + zc), np.float32(acc + ac))
+        Z, acc = _chains(e, v, 8 * c)
         R = np.float32(1) / Z
         o = np.float32(acc * R)
-        out[n, j] = _bf16(o)
         G = np.float32(R * _f(dout[n, j]))
         for k, (t, col, pos) in enumerate(members):
             a = np.float32(e[k] * G)
@@ -91,12 +123,12 @@ def case(request):
     dout = _bf16(rng.standard_normal((N, d)))
     ref_out = oracle.fwd_f32(kv, sc, ape, cu, T, r, c, d)
     dkv, dsc, dape, _, _ = oracle.bwd_f32(kv, sc, ape, cu, T, r, c, d, dout)
-    got = chunked_model(kv, sc, ape, dout, cu, T, r, c, d)
+    got = kernel_order_model(kv, sc, ape, dout, cu, T, r, c, d)
     unused = ~brute.consumed_mask(cu, T, r, c, d)
     return cu, T, r, c, d, kv, got, (ref_out, dkv, dsc, dape), unused
 
 
-def test_chunked_order_passes(case):
+def test_kernel_order_passes(case):
     cu, T, r, c, d, kv, got, ref, unused = case
     st = check_reordered(cu, T, r, c, d, kv, got, ref, unused)
     assert st["out_size"] > 0
@@ -130,8 +162,8 @@ def test_wrong_dape_fails(case):
 
 
 def test_reordering_is_visible_and_within_tolerance():
-    """On a larger pack the chunked order does change some bf16 results
-    (so the checks above are not vacuous), all within the contract."""
+    """On a larger pack the kernels' order does change some bf16 results (so
+    the checks above are not vacuous), all within the contract."""
     cu, T, c, d, r = [0, 1300, 2000, 4000], 4100, 2, 64, 128
     rng = np.random.default_rng(5)
     W = c * d
@@ -141,6 +173,6 @@ def test_reordering_is_visible_and_within_tolerance():
     ape = (0.02 * rng.standard_normal((r, W))).astype(np.float32)
     dout = _bf16(rng.standard_normal((N, d)))
     ref = (oracle.fwd_f32(kv, sc, ape, cu, T, r, c, d),) + oracle.bwd_f32(kv, sc, ape, cu, T, r, c, d, dout)[:3]
-    got = chunked_model(kv, sc, ape, dout, cu, T, r, c, d)
+    got = kernel_order_model(kv, sc, ape, dout, cu, T, r, c, d)
     st = check_reordered(cu, T, r, c, d, kv, got, ref, ~brute.consumed_mask(cu, T, r, c, d))
     assert st["dkv_differ"] + st["dscore_differ"] > 0
