@@ -314,6 +314,11 @@ def _r128_cases():
     # 160 KiB of LDS
     lengths = np.random.default_rng(2048).integers(0, 300, size=2048).tolist()
     cases.append((lengths, int(sum(lengths)) + 5, 2, 64, 970, False))
+    # segment lengths at and next to multiples of 128 (no tail, a 1-row tail,
+    # one row short of a block)
+    lengths = [128, 256, 384, 127, 129, 0, 1, 512, 255]
+    cases.append((lengths, int(sum(lengths)) + 3, 2, 128, 971, True))
+    cases.append((lengths, int(sum(lengths)), 1, 64, 972, False))
     return cases
 
 
@@ -345,6 +350,34 @@ def test_extreme_scores_and_subnormals(dev):
     dout = (dout.float() * 1e-36).to(torch.bfloat16)
     got = run_gpu(dev, cu, 128, 4, 2, 64, kv, sc, ape, dout, N)
     check_against_oracle(cu, 128, 4, 2, 64, kv, sc, ape, dout, got)
+
+
+@pytest.mark.parametrize("c", [2, 1])
+def test_ratio128_half_windows_far_apart(dev, c):
+    """ratio 128: one half of every window about 100 below the other (the
+    forward's rescale factor EXP(m_h - M) then underflows to a subnormal or
+    to zero) and wide score spreads; compared within the tolerance."""
+    d = 64
+    lengths = [384, 256, 200, 128, 700]
+    wl = inputs.custom("r128far", lengths, sum(lengths) + 9, 128, c, d, seed=13)
+    cu = list(wl.cu_seqlens)
+    T = wl.total_tokens
+    N = G.csa_compressor_total_comp(cu, 128)
+    kv, sc, ape, dout = inputs.make_tensors(wl, N)
+    f = sc.float()
+    if c == 2:
+        f[:, :d] -= 100.0                       # every window's previous-block half
+    else:
+        pos = torch.zeros(T, dtype=torch.long)
+        for s0, s1 in zip(cu[:-1], cu[1:]):
+            pos[s0:s1] = torch.arange(s1 - s0) % 128
+        f[pos < 64] -= 100.0                    # every window's first 64 rows
+    g = torch.Generator().manual_seed(5)
+    f = f * torch.where(torch.rand(f.shape, generator=g) < 0.3, 4.0, 1.0)
+    sc = f.to(torch.bfloat16)
+    for host in (True, False):
+        got = run_gpu(dev, cu, T, 128, c, d, kv, sc, ape, dout, N, host=host)
+        check_against_oracle(cu, T, 128, c, d, kv, sc, ape, dout, got, label=f"r128far_c{c}")
 
 
 def test_invalid_device_cu_seqlens_touches_nothing(dev):
