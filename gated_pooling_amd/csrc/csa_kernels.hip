@@ -527,6 +527,16 @@ __device__ __forceinline__ bool reg_segment_table(const SegParams& sp, RegTable&
   return __ballot(bad_len) == 0 && c0 == 0 && static_cast<int64_t>(cS) <= sp.T_cap && total == sp.N;
 }
 
+// Entry i of a table in global memory that no kernel writes while this one
+// runs (cu_seqlens, or the offsets seg_scan_kernel wrote before), read at a
+// wave-uniform index through the scalar cache (constant address space): the
+// row loop's lookups then wait on the scalar counter instead of the vector
+// memory counter, which would also wait for every prefetched window.
+__device__ __forceinline__ uint32_t scalar_entry(const int32_t* t, int i) {
+  using const_ptr = const __attribute__((address_space(4))) int32_t*;
+  return static_cast<uint32_t>(((const_ptr)t)[i]);
+}
+
 template <int TBL>
 struct UTable {
   const SegParams& sp;   // kTableArgs: entries straight from the kernel arguments
@@ -535,12 +545,14 @@ struct UTable {
   RegTable rt{0, 0, false};  // kTableLds with fewer than 64 segments: in registers
   __device__ __forceinline__ uint32_t cu_at(int i) const {
     if constexpr (TBL == kTableArgs) return static_cast<uint32_t>(sp.arg_cu[i]);
-    else if (TBL == kTableLds && rt.on) return static_cast<uint32_t>(__builtin_amdgcn_readlane(rt.cu, i));
+    else if constexpr (TBL == kTableGlobal) return scalar_entry(cu, i);
+    else if (rt.on) return static_cast<uint32_t>(__builtin_amdgcn_readlane(rt.cu, i));
     else return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(cu[i]));
   }
   __device__ __forceinline__ uint32_t off_at(int i) const {
     if constexpr (TBL == kTableArgs) return static_cast<uint32_t>(sp.arg_off[i]);
-    else if (TBL == kTableLds && rt.on) return static_cast<uint32_t>(__builtin_amdgcn_readlane(rt.off, i));
+    else if constexpr (TBL == kTableGlobal) return scalar_entry(off, i);
+    else if (rt.on) return static_cast<uint32_t>(__builtin_amdgcn_readlane(rt.off, i));
     else return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(off[i]));
   }
 };
